@@ -1,0 +1,52 @@
+// Internal declarations shared by the host logic (host.cpp, plain C++) and the
+// HIP launchers (*.hip).  Not part of the ABI.
+#pragma once
+
+#include <cstdint>
+#include <string>
+
+#include "cpattn.h"
+
+namespace cpattn {
+
+// Forward tile geometry.  A workgroup is 4 wave64s; each wave owns 32 query
+// rows of one head.  hpw heads of one GQA group share a workgroup (and every
+// K/V tile it stages), so a workgroup covers bm = 128 / hpw query rows.
+struct TileGeom {
+    int bm;   // query rows per workgroup tile
+    int bn;   // keys per K/V tile
+    int hpw;  // query heads per workgroup (divides Hq / Hkv)
+};
+TileGeom fwd_geom(int hq, int hkv);
+
+// Backward geometry: a workgroup owns bnk keys of one KV head (32 per wave)
+// and walks query tiles of bmq rows.
+constexpr int kBwdKeysPerWG = 128;
+constexpr int kBwdQRows = 32;
+
+void set_error(const std::string& msg);
+cp_status fail(cp_status s, const std::string& msg);
+
+// Validate a problem.  device_docs: cu_seqlens will be read by a kernel (only
+// its presence is checked) rather than on the host (where it is also checked
+// for monotonicity and range).
+cp_status validate_problem(const cp_attn_problem* p, bool device_docs);
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Tile-range rule shared by the host block map and (as a mirror in device
+// code) the forward kernel.  For a query tile [q0, q1] (global positions, q1
+// the last row) and a KV segment starting at kpos0 with klen keys in tiles of
+// bn: visited tiles are [t_lo, t_hi).  lo0 / lo1 are the first visible key
+// position of rows q0 / q1 (document start for DOC, unbounded otherwise).
+struct TileRange {
+    int64_t t_lo, t_hi;
+};
+TileRange tile_range(int mask, int64_t q0, int64_t q1, int64_t lo0, int64_t kpos0, int64_t klen, int bn);
+// Class of tile t inside the visited range.
+int tile_class(int mask, int64_t q0, int64_t q1, int64_t lo1, int64_t kpos0, int64_t klen, int bn, int64_t t);
+
+// Document start of a global position (host cu_seqlens).
+int64_t doc_start_host(const int32_t* cu, int32_t n_docs, int64_t pos);
+
+}  // namespace cpattn

@@ -1,0 +1,205 @@
+"""Host ring scheduler: replays one rank's Pass-KV ring steps on one GPU.
+
+Pass KV keeps the rank's queries in place while KV blocks travel one hop per
+step around the ring; each step runs the attention kernel on the local queries
+and the block just received, and the partial outputs are merged ("Context
+Parallelism for Scalable Million-Token Inference", section "Ring Attention
+Algorithms"; "Announcing Long-Context Training on TPUs with MaxText Context
+Parallelism", section "Context Parallelism in MaxText", P2P paragraph).
+
+On one GPU there is no neighbour to receive from: every source rank's block
+already sits in HBM, and a copy on a side stream into a double-buffered
+receive buffer stands in for the transfer that would run under the kernel.
+All arithmetic runs in libcpattn (``cpattn``); torch only provides device
+memory, streams and events.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import torch
+
+from . import cpattn
+from .inputs import Workload
+
+
+class RingScheduleError(RuntimeError):
+    """A ring schedule that does not visit every source rank exactly once."""
+
+
+@dataclasses.dataclass
+class StepResult:
+    step: int
+    source: int
+    masks: list
+
+
+def check_schedule(cp_size: int, sources) -> None:
+    """Reject a schedule that drops or repeats a source before anything is merged."""
+    seen = sorted(int(s) for s in sources)
+    if seen != list(range(cp_size)):
+        raise RingScheduleError(f"ring schedule visits sources {seen}, expected each of 0..{cp_size - 1} once")
+
+
+class RankRing:
+    """One rank's share of a context-parallel sequence of ``w.seq_len`` tokens."""
+
+    def __init__(self, w: Workload, rank: int, cu_seqlens: np.ndarray | None = None, device="cuda"):
+        self.w = w
+        self.rank = rank
+        self.R = w.cp
+        self.c = w.chunk
+        self.device = torch.device(device)
+        self.pos = cpattn.cp_partition_zigzag(w.seq_len, w.cp, rank)
+        self.packed = cu_seqlens is not None
+        if self.packed:
+            self.cu_host = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
+            self.cu_dev = torch.from_numpy(self.cu_host).to(self.device)
+            self.n_docs = len(self.cu_host) - 1
+        else:
+            self.cu_host = None
+            self.cu_dev = None
+            self.n_docs = 0
+
+    # ------------------------------------------------------------- problems
+    def chunks_of(self, r: int) -> tuple[int, int]:
+        pos = cpattn.cp_partition_zigzag(self.w.seq_len, self.R, r)
+        return int(pos[0]) // self.c, int(pos[self.c]) // self.c
+
+    def schedule(self) -> list[int]:
+        return [cpattn.cp_ring_source(self.R, self.rank, t) for t in range(self.R)]
+
+    def problem(self, step: int, source: int | None = None, host_docs: bool = False) -> cpattn.cp_attn_problem:
+        w, c = self.w, self.c
+        src = cpattn.cp_ring_source(self.R, self.rank, step) if source is None else source
+        qa, qb = self.chunks_of(self.rank)
+        ka, kb = self.chunks_of(src)
+        masks = cpattn.cp_step_masks(self.R, self.rank, step, self.packed)
+        cu_ptr, n_docs = None, 0
+        if self.packed:
+            cu_ptr = self.cu_host.ctypes.data if host_docs else self.cu_dev.data_ptr()
+            n_docs = self.n_docs
+        return cpattn.make_problem(w.hq, w.hkv, w.dim, w.scale, 2 * c, 2 * c,
+                                   [(0, qa * c, c), (c, qb * c, c)], [(0, ka * c, c), (c, kb * c, c)],
+                                   masks, cu_ptr, n_docs)
+
+    def step_pairs(self, step: int) -> int:
+        """Visible (query, key) pairs per query head at ``step`` (host count)."""
+        return cpattn.cp_count_pairs(self.problem(step, host_docs=True))
+
+    # ------------------------------------------------------------- forward
+    def forward(self, q, kv_of_source, stage: bool = True, keep_steps: bool = False, schedule=None,
+                timer=None):
+        """Run the rank's forward ring.
+
+        q: device bf16 [2c, Hq, D]; kv_of_source(src) -> (k, v) device bf16 [2c, Hkv, D].
+        Returns (O fp32 [2c, Hq, D], LSE fp32 [Hq, 2c], per-step partials if keep_steps).
+        ``timer`` (optional) is called as timer(step, "fwd_begin"/"fwd_end", stream).
+        """
+        w = self.w
+        rows = 2 * self.c
+        sched = self.schedule() if schedule is None else list(schedule)
+        check_schedule(self.R, sched)
+        dev = self.device
+        o_acc = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
+        lse_acc = torch.full((w.hq, rows), float("-inf"), dtype=torch.float32, device=dev)
+        o_t = torch.empty_like(o_acc)
+        lse_t = torch.empty_like(lse_acc)
+        steps = []
+        compute = torch.cuda.current_stream(dev)
+        feeder = _Feeder(kv_of_source, sched, stage, dev)
+        for t, src in enumerate(sched):
+            k, v = feeder.get(t, compute)
+            p = self.problem(t, src)
+            if timer:
+                timer(t, "fwd_begin", compute)
+            cpattn.cp_attn_fwd_step(p, q, k, v, o_t, lse_t, stream=compute)
+            if timer:
+                timer(t, "fwd_end", compute)
+            feeder.release(t, compute)
+            if keep_steps:
+                steps.append((o_t.clone(), lse_t.clone()))
+            cpattn.cp_merge_partials(o_acc, lse_acc, o_t, lse_t, rows, w.hq, w.dim, stream=compute)
+        return o_acc, lse_acc, steps
+
+    # ------------------------------------------------------------- backward
+    def backward(self, q, d_o, o, lse, kv_of_source, stage: bool = True, schedule=None, keep_steps=True,
+                 timer=None):
+        """Run the rank's backward ring from the final O and LSE.
+
+        Returns (dQ fp32 [2c, Hq, D], per-step list of (source, dK_t, dV_t) fp32 [2c, Hkv, D]).
+        With keep_steps=False only the last step's dK/dV buffers are kept (benchmarking).
+        """
+        w = self.w
+        rows = 2 * self.c
+        sched = self.schedule() if schedule is None else list(schedule)
+        check_schedule(self.R, sched)
+        dev = self.device
+        compute = torch.cuda.current_stream(dev)
+        delta = torch.empty((w.hq, rows), dtype=torch.float32, device=dev)
+        cpattn.cp_attn_bwd_prep(d_o, o, delta, rows, w.hq, w.dim, stream=compute)
+        dq = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
+        out = []
+        feeder = _Feeder(kv_of_source, sched, stage, dev)
+        dk = dv = None
+        for t, src in enumerate(sched):
+            k, v = feeder.get(t, compute)
+            if keep_steps or dk is None:
+                dk = torch.empty((rows, w.hkv, w.dim), dtype=torch.float32, device=dev)
+                dv = torch.empty_like(dk)
+            p = self.problem(t, src)
+            if timer:
+                timer(t, "bwd_begin", compute)
+            cpattn.cp_attn_bwd_step(p, q, k, v, d_o, lse, delta, dq, dk, dv, stream=compute)
+            if timer:
+                timer(t, "bwd_end", compute)
+            feeder.release(t, compute)
+            out.append((src, dk, dv))
+        return dq, out
+
+
+class _Feeder:
+    """Supplies the KV block of each step, optionally through a double-buffered
+    receive buffer filled on a side stream (the stand-in for the ring transfer)."""
+
+    def __init__(self, kv_of_source, sched, stage, dev):
+        self.kv_of_source = kv_of_source
+        self.sched = sched
+        self.stage = stage
+        self.dev = dev
+        if stage:
+            self.side = torch.cuda.Stream(dev)
+            self.buf = [None, None]
+            self.ready = [torch.cuda.Event(), torch.cuda.Event()]
+            self.free = [torch.cuda.Event(), torch.cuda.Event()]
+            self.free_recorded = [False, False]
+            self._issue(0)
+
+    def _issue(self, t):
+        k_src, v_src = self.kv_of_source(self.sched[t])
+        slot = t % 2
+        if self.buf[slot] is None:
+            self.buf[slot] = (torch.empty_like(k_src), torch.empty_like(v_src))
+        kb, vb = self.buf[slot]
+        with torch.cuda.stream(self.side):
+            if self.free_recorded[slot]:
+                self.side.wait_event(self.free[slot])
+            kb.copy_(k_src, non_blocking=True)
+            vb.copy_(v_src, non_blocking=True)
+            self.ready[slot].record(self.side)
+
+    def get(self, t, compute):
+        if not self.stage:
+            return self.kv_of_source(self.sched[t])
+        slot = t % 2
+        compute.wait_event(self.ready[slot])
+        if t + 1 < len(self.sched):
+            self._issue(t + 1)
+        return self.buf[slot]
+
+    def release(self, t, compute):
+        if self.stage:
+            slot = t % 2
+            self.free[slot].record(compute)
+            self.free_recorded[slot] = True

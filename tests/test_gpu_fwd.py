@@ -1,0 +1,191 @@
+"""GPU parity of the forward ring step, the merge and the kernel's own block map
+against the float64 oracle, through the C ABI (libcpattn.so)."""
+import numpy as np
+import pytest
+
+import oracle
+from context_long_attention_amd import inputs
+from tests.gpu_common import RankInputs, assert_lse_close, assert_o_close, device_bf16, note
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from context_long_attention_amd import cpattn
+    cpattn.lib()
+
+
+def _ring(w, rank, cu=None):
+    from context_long_attention_amd.ring import RankRing
+    return RankRing(w, rank, cu)
+
+
+def _oracle_blocks(inp, ring):
+    return [inp.kv64[s] for s in ring.schedule()]
+
+
+def _check_rank(w, rank, cu=None, check_steps=True, check_map=True):
+    from context_long_attention_amd import cpattn
+    note(f"fwd {w.name} S={w.seq_len} R={w.cp} Hq={w.hq} Hkv={w.hkv} D={w.dim} rank={rank} docs={cu is not None}")
+    inp = RankInputs(w, rank)
+    ring = _ring(w, rank, cu)
+    o, lse, steps = ring.forward(inp.q, inp.kv_of_source, stage=True, keep_steps=True)
+    torch.cuda.synchronize()
+    ro, rlse, rsteps = oracle.rank_forward(inp.q64, inp.qpos, _oracle_blocks(inp, ring), cu, w.scale)
+    live = np.isfinite(rlse).T  # [rows, Hq]
+    assert_o_close(o.cpu().numpy(), ro, f"merged O rank {rank}", live)
+    assert_lse_close(lse.cpu().numpy(), rlse, f"merged LSE rank {rank}")
+    if check_steps:
+        for t, ((ot, lt), (rot, rlt)) in enumerate(zip(steps, rsteps)):
+            assert_o_close(ot.cpu().numpy(), rot, f"O_t rank {rank} step {t}", np.isfinite(rlt).T)
+            assert_lse_close(lt.cpu().numpy(), rlt, f"LSE_t rank {rank} step {t}")
+    if check_map:
+        bm, bn = cpattn.cp_tile_shape(w.hq, w.hkv, w.dim)
+        for t in range(w.cp):
+            p = ring.problem(t)
+            nq, nk = cpattn.cp_block_map_size(p)
+            tm = torch.full((nq, nk), 255, dtype=torch.uint8, device="cuda")
+            k, v = inp.kv_of_source(ring.schedule()[t])
+            o_t = torch.empty((w.local, w.hq, w.dim), dtype=torch.float32, device="cuda")
+            l_t = torch.empty((w.hq, w.local), dtype=torch.float32, device="cuda")
+            cpattn.cp_attn_fwd_step(p, inp.q, k, v, o_t, l_t, tile_map=tm)
+            got = tm.cpu().numpy()
+            qseg = [(int(p.q_seg[i].pos0), int(p.q_seg[i].len)) for i in range(p.n_q_seg)]
+            kseg = [(int(p.kv_seg[j].pos0), int(p.kv_seg[j].len)) for j in range(p.n_kv_seg)]
+            ref = oracle.tile_map(qseg, kseg, bm, bn, cu)
+            assert np.array_equal(got, ref), f"kernel block map differs at step {t}"
+            assert np.array_equal(cpattn.cp_block_map(ring.problem(t, host_docs=True)), ref)
+    return o, lse
+
+
+def test_tiny_every_rank_and_step():
+    """The tiny workload on all 4 ranks x 4 steps; scattered outputs equal full attention."""
+    w = inputs.WORKLOADS["tiny"]
+    o_glob = np.zeros((w.seq_len, w.hq, w.dim))
+    l_glob = np.zeros((w.hq, w.seq_len))
+    q_all = None
+    for r in range(w.cp):
+        o, lse = _check_rank(w, r)
+        pos = oracle.zigzag_positions(w.seq_len, w.cp, r)
+        o_glob[pos] = o.cpu().numpy()
+        l_glob[:, pos] = lse.cpu().numpy()
+    c = w.chunk
+    q = inputs.round_bf16(inputs.chunks_normal(inputs.SEED_Q, range(2 * w.cp), c, w.hq, w.dim)).astype(np.float64)
+    k = inputs.round_bf16(inputs.chunks_normal(inputs.SEED_K, range(2 * w.cp), c, w.hkv, w.dim)).astype(np.float64)
+    v = inputs.round_bf16(inputs.chunks_normal(inputs.SEED_V, range(2 * w.cp), c, w.hkv, w.dim)).astype(np.float64)
+    pos = np.arange(w.seq_len)
+    ro, rl = oracle.attention_partial(q, k, v, oracle.visibility(pos, pos), w.scale)
+    assert_o_close(o_glob, ro, "tiny scattered O")
+    assert_lse_close(l_glob, rl, "tiny scattered LSE")
+    del q_all
+
+
+RAGGED = [
+    # name, S, R, Hq, Hkv, D   (chunk lengths that are not multiples of the tiles)
+    ("g4_d128", 2 * 2 * 100, 2, 8, 2, 128),
+    ("g1_d64", 2 * 3 * 77, 3, 4, 4, 64),
+    ("g2_d128", 2 * 2 * 90, 2, 6, 3, 128),
+    ("g16_d64", 2 * 4 * 33, 4, 16, 1, 64),
+    ("g8_d128", 2 * 2 * 130, 2, 8, 1, 128),
+    ("g3_d64", 2 * 2 * 70, 2, 6, 2, 64),
+]
+
+
+@pytest.mark.parametrize("name,S,R,hq,hkv,d", RAGGED, ids=[r[0] for r in RAGGED])
+def test_ragged_shapes(name, S, R, hq, hkv, d):
+    w = inputs.Workload(name, S, R, hq, hkv, d, backward=False)
+    for r in sorted({0, R - 1}):
+        _check_rank(w, r)
+
+
+def test_packed_documents_small():
+    cu = np.array([0, 1, 2, 130, 131, 300, 301, 520, 767, 768], dtype=np.int32)
+    w = inputs.Workload("packed_small", 768, 4, 8, 2, 128, backward=False, packed=True)
+    for r in range(w.cp):
+        _check_rank(w, r, cu)
+
+
+def test_single_token_chunks():
+    """c = 1: every chunk is one token (the pages' 4-token, 2-rank example shape)."""
+    w = inputs.Workload("c1", 4, 2, 4, 2, 64, backward=False)
+    for r in range(2):
+        _check_rank(w, r)
+
+
+def test_empty_and_skip_segments():
+    """An empty KV segment, an empty query segment and an all-SKIP step."""
+    from context_long_attention_amd import cpattn
+    hq, hkv, d = 4, 2, 128
+    n = 96
+    q64, q = device_bf16(inputs.chunk_normal(1, 0, n, hq, d))
+    k64, k = device_bf16(inputs.chunk_normal(2, 0, n, hkv, d))
+    v64, v = device_bf16(inputs.chunk_normal(3, 0, n, hkv, d))
+    o = torch.full((n, hq, d), 7.0, device="cuda")
+    lse = torch.full((hq, n), 7.0, device="cuda")
+    F, D_, S_ = cpattn.CP_MASK_FULL, cpattn.CP_MASK_DIAG_CAUSAL, cpattn.CP_MASK_SKIP
+    # query rows [0, 96) at positions 1000..; KV segment 0 empty, segment 1 = rows [0, 96) at 1000..
+    p = cpattn.make_problem(hq, hkv, d, 0.125, n, n, [(0, 1000, n)], [(0, 0, 0), (0, 1000, n)], [[F, D_], [S_, S_]])
+    cpattn.cp_attn_fwd_step(p, q, k, v, o, lse)
+    pos = np.arange(1000, 1000 + n)
+    ro, rl = oracle.attention_partial(q64, k64, v64, oracle.visibility(pos, pos), 0.125)
+    assert_o_close(o.cpu().numpy(), ro, "empty KV segment O")
+    assert_lse_close(lse.cpu().numpy(), rl, "empty KV segment LSE")
+    # all SKIP: every row gets (0, -inf)
+    p = cpattn.make_problem(hq, hkv, d, 0.125, n, n, [(0, 0, 48), (48, 48, 48)], [(0, 500, n)], [[S_, S_], [S_, S_]])
+    cpattn.cp_attn_fwd_step(p, q, k, v, o, lse)
+    assert torch.all(o == 0).item() and torch.all(torch.isneginf(lse)).item()
+    # an empty query segment writes nothing
+    o.fill_(7.0)
+    p = cpattn.make_problem(hq, hkv, d, 0.125, n, n, [(0, 0, 0)], [(0, 0, n)], [[F, F], [F, F]])
+    cpattn.cp_attn_fwd_step(p, q, k, v, o, lse)
+    torch.cuda.synchronize()
+    assert torch.all(o == 7.0).item()
+
+
+def test_merge_kernel_matches_oracle():
+    from context_long_attention_amd import cpattn
+    rng = np.random.default_rng(3)
+    rows, hq, d = 300, 6, 64
+    o1, o2 = rng.standard_normal((rows, hq, d)), rng.standard_normal((rows, hq, d))
+    l1, l2 = rng.standard_normal((hq, rows)) * 5, rng.standard_normal((hq, rows)) * 5
+    l1[0, :10] = -np.inf
+    l2[0, 5:15] = -np.inf
+    o1[:, 0][np.isneginf(l1[0])] = 0
+    o2[:, 0][np.isneginf(l2[0])] = 0
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device="cuda")
+    oa, la, ob, lb = t(o1), t(l1), t(o2), t(l2)
+    cpattn.cp_merge_partials(oa, la, ob, lb, rows, hq, d)
+    ro, rl = oracle.merge(np.float32(o1), np.float32(l1), np.float32(o2), np.float32(l2))
+    np.testing.assert_allclose(oa.cpu().numpy(), ro, atol=1e-5)
+    got_l = la.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(rl))
+    np.testing.assert_allclose(got_l[np.isfinite(rl)], rl[np.isfinite(rl)], atol=1e-5)
+
+
+def _sampled_rows(local, c, n_extra, seed):
+    rng = np.random.default_rng(seed)
+    edge = [0, 1, 2, c - 1, c, c + 1, local - 2, local - 1]
+    return np.unique(np.concatenate([edge, rng.integers(0, local, n_extra)]))
+
+
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("rank", [0, 7])
+def test_llama3_8b_forward_full_size_sampled(rank):
+    """Llama-3-8B shape, one rank's share of S=128K at CP=8: the whole ring on the GPU,
+    compared on sampled rows (all heads, every key) with the oracle."""
+    w = inputs.WORKLOADS["llama3_8b_fwd"]
+    note(f"fwd {w.name} full size rank={rank}")
+    inp = RankInputs(w, rank)
+    ring = _ring(w, rank)
+    o, lse, _ = ring.forward(inp.q, inp.kv_of_source, stage=True)
+    torch.cuda.synchronize()
+    rows = _sampled_rows(w.local, w.chunk, 40, rank)
+    ro, rl, _ = oracle.rank_forward(inp.q64, inp.qpos, _oracle_blocks(inp, ring), None, w.scale, rows=rows)
+    assert_o_close(o[rows].cpu().numpy(), ro, f"O rank {rank}")
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, f"LSE rank {rank}")
+    assert not torch.isnan(o).any().item()

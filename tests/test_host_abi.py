@@ -1,0 +1,172 @@
+"""CPU tests of libcpattn.so: it loads, exports every symbol include/cpattn.h
+declares, its host integer logic (partition, ring order, chunk classes, block
+map, pair counts) is bit-exact against the oracle's brute force, and bad
+arguments are rejected before any launch.  No kernel runs here."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from context_long_attention_amd import cpattn
+from context_long_attention_amd.ring import RankRing, RingScheduleError, check_schedule
+from context_long_attention_amd import inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "cpattn.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return cpattn.lib()
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(cp_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared()
+    assert len(declared) >= 14
+    assert sorted(cpattn.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    version = int(re.search(r"#define CPATTN_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert cpattn.cp_abi_version() == version
+    assert cpattn.cp_status_string(cpattn.CP_ERR_UNSUPPORTED) == "unsupported"
+
+
+@pytest.mark.parametrize("S,R", [(4, 2), (16, 2), (24, 3), (64, 4), (80, 5), (512, 4), (2048, 16)])
+def test_partition_bit_exact(S, R):
+    for r in range(R):
+        got = cpattn.cp_partition_zigzag(S, R, r)
+        assert got.dtype == np.int64
+        assert np.array_equal(got, oracle.zigzag_positions(S, R, r))
+        for t in range(R):
+            assert cpattn.cp_ring_source(R, r, t) == oracle.ring_source(r, t, R)
+
+
+def test_partition_errors():
+    with pytest.raises(cpattn.CpError) as e:
+        cpattn.cp_partition_zigzag(10, 3, 0)
+    assert e.value.status == cpattn.CP_ERR_INVALID_ARG
+    with pytest.raises(cpattn.CpError):
+        cpattn.cp_partition_zigzag(16, 2, 2)
+    with pytest.raises(cpattn.CpError):
+        cpattn.cp_ring_source(4, 0, 4)
+
+
+@pytest.mark.parametrize("S,R", [(16, 2), (24, 3), (64, 4), (80, 5), (512, 4)])
+def test_step_masks_match_brute_force(S, R):
+    c = S // (2 * R)
+    cu = np.array([0, 3, 3, S // 2 + 1, S], dtype=np.int32)
+    for r in range(R):
+        qpos = oracle.zigzag_positions(S, R, r)
+        for t in range(R):
+            kpos = oracle.zigzag_positions(S, R, oracle.ring_source(r, t, R))
+            for packed in (False, True):
+                got = cpattn.cp_step_masks(R, r, t, packed)
+                for i in range(2):
+                    for j in range(2):
+                        ref = oracle.chunk_pair_class(qpos[i * c:(i + 1) * c], kpos[j * c:(j + 1) * c],
+                                                      cu if packed else None)
+                        if packed and ref == oracle.CLS_SKIP:
+                            # DOC may still be chosen when the chunks are causal-visible but
+                            # documents cut them apart; SKIP must be exact in the causal case
+                            assert got[i][j] in (oracle.CLS_SKIP, oracle.CLS_DOC)
+                        else:
+                            assert got[i][j] == ref, (r, t, i, j, packed)
+
+
+MAP_CASES = [
+    # S, R, Hq, Hkv, D, packed
+    (400, 2, 8, 2, 128, False),
+    (462, 3, 4, 4, 64, False),
+    (360, 2, 6, 3, 128, True),
+    (264, 4, 16, 1, 64, True),
+    (1024, 4, 8, 2, 128, True),
+]
+
+
+@pytest.mark.parametrize("S,R,hq,hkv,d,packed", MAP_CASES)
+def test_block_map_and_pairs_match_brute_force(S, R, hq, hkv, d, packed):
+    cu = None
+    if packed:
+        cu = np.array([0, 1, 2, S // 3, S // 3 + 1, S // 2, S - 1, S], dtype=np.int32)
+    w = inputs.Workload("case", S, R, hq, hkv, d, backward=False)
+    bm, bn = cpattn.cp_tile_shape(hq, hkv, d)
+    assert bn == 64 and bm in (32, 64, 128)
+    for r in range(R):
+        ring = RankRing(w, r, cu, device="cpu")
+        for t in range(R):
+            p = ring.problem(t, host_docs=True)
+            qseg = [(int(p.q_seg[i].pos0), int(p.q_seg[i].len)) for i in range(p.n_q_seg)]
+            kseg = [(int(p.kv_seg[j].pos0), int(p.kv_seg[j].len)) for j in range(p.n_kv_seg)]
+            ref = oracle.tile_map(qseg, kseg, bm, bn, cu)
+            assert np.array_equal(cpattn.cp_block_map(p), ref), (r, t)
+            qpos = ring.pos
+            kpos = cpattn.cp_partition_zigzag(S, R, ring.schedule()[t])
+            assert cpattn.cp_count_pairs(p) == int(oracle.visibility(qpos, kpos, cu).sum())
+
+
+def test_validation_rejects_bad_problems(lib):
+    F = cpattn.CP_MASK_FULL
+    good = dict(hq=4, hkv=2, head_dim=128, scale=0.1, q_rows=64, kv_rows=64,
+                q_segments=[(0, 0, 64)], kv_segments=[(0, 0, 64)], masks=[[F, F], [F, F]])
+
+    def status(**over):
+        kw = dict(good)
+        kw.update(over)
+        p = cpattn.make_problem(**kw)
+        a, b = ctypes.c_int64(), ctypes.c_int64()
+        return lib.cp_block_map_size(ctypes.byref(p), ctypes.byref(a), ctypes.byref(b))
+
+    assert status() == cpattn.CP_OK
+    assert status(head_dim=96) == cpattn.CP_ERR_UNSUPPORTED
+    assert status(hq=6, hkv=4) == cpattn.CP_ERR_INVALID_ARG
+    assert status(q_segments=[(0, 0, 65)]) == cpattn.CP_ERR_INVALID_ARG
+    assert status(q_segments=[(0, 0, 40), (30, 100, 20)]) == cpattn.CP_ERR_INVALID_ARG
+    assert status(kv_segments=[(10, 0, 60)]) == cpattn.CP_ERR_INVALID_ARG
+    assert status(masks=[[7, F], [F, F]]) == cpattn.CP_ERR_INVALID_ARG
+    assert status(masks=[[cpattn.CP_MASK_DOC, F], [F, F]]) == cpattn.CP_ERR_INVALID_ARG  # no cu_seqlens
+    assert status(scale=float("inf")) == cpattn.CP_ERR_INVALID_ARG
+    # device entry points validate before any HIP call: these return without launching
+    p = cpattn.make_problem(**dict(good, head_dim=80))
+    assert lib.cp_attn_fwd_step(ctypes.byref(p), None, None, None, None, None, None, None) == cpattn.CP_ERR_UNSUPPORTED
+    assert lib.cp_attn_bwd_step(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
+                                None) == cpattn.CP_ERR_UNSUPPORTED
+    assert lib.cp_merge_partials(None, None, None, None, -1, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_merge_partials(None, None, None, None, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_attn_bwd_prep(None, None, None, 10, 4, 72, None) == cpattn.CP_ERR_UNSUPPORTED
+    assert b"head_dim" in lib.cp_last_error()
+
+
+def test_host_cu_seqlens_checked(lib):
+    D = cpattn.CP_MASK_DOC
+    cu = np.array([0, 10, 5, 64], dtype=np.int32)  # not monotone
+    p = cpattn.make_problem(4, 2, 64, 0.1, 64, 64, [(0, 0, 64)], [(0, 0, 64)], [[D, D], [D, D]],
+                            cu.ctypes.data, 3)
+    with pytest.raises(cpattn.CpError):
+        cpattn.cp_block_map(p)
+    cu2 = np.array([0, 10, 20], dtype=np.int32)  # does not cover position 63
+    p = cpattn.make_problem(4, 2, 64, 0.1, 64, 64, [(0, 0, 64)], [(0, 0, 64)], [[D, D], [D, D]],
+                            cu2.ctypes.data, 2)
+    with pytest.raises(cpattn.CpError):
+        cpattn.cp_count_pairs(p)
+
+
+def test_schedule_check_rejects_dropped_or_repeated_steps():
+    check_schedule(4, [0, 3, 2, 1])
+    with pytest.raises(RingScheduleError):
+        check_schedule(4, [0, 3, 3, 1])
+    with pytest.raises(RingScheduleError):
+        check_schedule(4, [0, 3, 2])
+    w = inputs.WORKLOADS["tiny"]
+    ring = RankRing(w, 1, device="cpu")
+    assert ring.schedule() == [oracle.ring_source(1, t, 4) for t in range(4)]
+    with pytest.raises(RingScheduleError):
+        ring.forward(None, None, schedule=[1, 0, 0, 2])
