@@ -170,6 +170,10 @@ class _Feeder:
         self.dev = dev
         if stage:
             self.side = torch.cuda.Stream(dev)
+            # The receive buffers come from torch's caching allocator, which may hand
+            # back blocks whose previous users are still queued on the compute stream:
+            # the first copy must not start before that earlier work.
+            self.side.wait_stream(torch.cuda.current_stream(dev))
             self.buf = [None, None]
             self.ready = [torch.cuda.Event(), torch.cuda.Event()]
             self.free = [torch.cuda.Event(), torch.cuda.Event()]
@@ -180,7 +184,11 @@ class _Feeder:
         k_src, v_src = self.kv_of_source(self.sched[t])
         slot = t % 2
         if self.buf[slot] is None:
-            self.buf[slot] = (torch.empty_like(k_src), torch.empty_like(v_src))
+            kb, vb = torch.empty_like(k_src), torch.empty_like(v_src)
+            # written on the side stream: keep the blocks until its work is done
+            kb.record_stream(self.side)
+            vb.record_stream(self.side)
+            self.buf[slot] = (kb, vb)
         kb, vb = self.buf[slot]
         with torch.cuda.stream(self.side):
             if self.free_recorded[slot]:

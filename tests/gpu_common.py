@@ -57,8 +57,13 @@ def assert_o_close(got: np.ndarray, ref: np.ndarray, what: str, live=None):
     if live is not None:
         g = g[live]
         ref = ref[live]
-    err = float(np.max(np.abs(g - ref))) if g.size else 0.0
-    assert err <= O_ATOL, f"{what}: max abs err {err:.3e} > {O_ATOL}"
+    diff = np.abs(g - ref)
+    err = float(diff.max()) if g.size else 0.0
+    if err > O_ATOL:
+        where = np.unravel_index(int(np.argmax(diff)), diff.shape)
+        bad = int((diff > O_ATOL).sum())
+        raise AssertionError(f"{what}: max abs err {err:.3e} > {O_ATOL} at {tuple(int(x) for x in where)} "
+                             f"(got {g[where]:.4e}, want {ref[where]:.4e}; {bad} of {diff.size} elements off)")
     return err
 
 

@@ -1,0 +1,145 @@
+"""GPU parity of the backward ring step (and delta preprocessing) against the
+float64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from context_long_attention_amd import inputs
+from tests.gpu_common import RankInputs, assert_lse_close, assert_o_close, note
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from context_long_attention_amd import cpattn
+    cpattn.lib()
+
+
+def _run(w, rank, cu=None):
+    from context_long_attention_amd.ring import RankRing
+    note(f"bwd {w.name} S={w.seq_len} R={w.cp} Hq={w.hq} Hkv={w.hkv} D={w.dim} rank={rank} docs={cu is not None}")
+    inp = RankInputs(w, rank, want_do=True)
+    ring = RankRing(w, rank, cu)
+    o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
+    dq, per_step = ring.backward(inp.q, inp.do, o, lse, inp.kv_of_source)
+    torch.cuda.synchronize()
+    return inp, ring, o, lse, dq, per_step
+
+
+def _check_rank(w, rank, cu=None):
+    inp, ring, o, lse, dq, per_step = _run(w, rank, cu)
+    blocks = [inp.kv64[s] for s in ring.schedule()]
+    ro, rl, _ = oracle.rank_forward(inp.q64, inp.qpos, blocks, cu, w.scale)
+    rdq, rsteps, rdelta = oracle.rank_backward(inp.q64, inp.qpos, inp.do64, ro, rl, blocks, cu, w.scale)
+    assert_o_close(dq.cpu().numpy(), rdq, f"dQ rank {rank}")
+    for t, ((src, dk, dv), (rdk, rdv)) in enumerate(zip(per_step, rsteps)):
+        assert src == ring.schedule()[t]
+        assert_o_close(dk.cpu().numpy(), rdk, f"dK rank {rank} step {t}")
+        assert_o_close(dv.cpu().numpy(), rdv, f"dV rank {rank} step {t}")
+    return dq, per_step
+
+
+def test_delta_kernel():
+    from context_long_attention_amd import cpattn
+    from tests.gpu_common import device_bf16
+    rows, hq, d = 130, 3, 128
+    do64, do = device_bf16(inputs.chunk_normal(4, 0, rows, hq, d))
+    o = np.random.default_rng(1).standard_normal((rows, hq, d)).astype(np.float32)
+    delta = torch.empty((hq, rows), device="cuda")
+    cpattn.cp_attn_bwd_prep(do, torch.from_numpy(o).cuda(), delta, rows, hq, d)
+    np.testing.assert_allclose(delta.cpu().numpy(), oracle.delta_rows(do64, o), atol=1e-4)
+
+
+def test_tiny_every_rank_sums_to_full_gradient():
+    """All 4 ranks x 4 steps of the tiny workload: per-step dK/dV and local dQ match
+    the oracle, and the per-source sums equal the full-sequence gradients."""
+    w = inputs.WORKLOADS["tiny"]
+    S, R, c = w.seq_len, w.cp, w.chunk
+    dq_g = np.zeros((S, w.hq, w.dim))
+    dk_g = np.zeros((S, w.hkv, w.dim))
+    dv_g = np.zeros((S, w.hkv, w.dim))
+    for r in range(R):
+        dq, per_step = _check_rank(w, r)
+        dq_g[oracle.zigzag_positions(S, R, r)] = dq.cpu().numpy()
+        for src, dk, dv in per_step:
+            kpos = oracle.zigzag_positions(S, R, src)
+            dk_g[kpos] += dk.cpu().numpy()
+            dv_g[kpos] += dv.cpu().numpy()
+    rb = lambda seed, h: inputs.round_bf16(inputs.chunks_normal(seed, range(2 * R), c, h, w.dim)).astype(np.float64)
+    q, k, v, do = rb(inputs.SEED_Q, w.hq), rb(inputs.SEED_K, w.hkv), rb(inputs.SEED_V, w.hkv), rb(inputs.SEED_DO, w.hq)
+    pos = np.arange(S)
+    vis = oracle.visibility(pos, pos)
+    o, lse = oracle.attention_partial(q, k, v, vis, w.scale)
+    rdq, rdk, rdv = oracle.attention_backward_partial(q, k, v, do, lse, oracle.delta_rows(do, o), vis, w.scale)
+    assert_o_close(dq_g, rdq, "full dQ")
+    assert_o_close(dk_g, rdk, "full dK")
+    assert_o_close(dv_g, rdv, "full dV")
+
+
+RAGGED = [
+    ("g4_d128", 2 * 2 * 100, 2, 8, 2, 128),
+    ("g1_d64", 2 * 3 * 77, 3, 4, 4, 64),
+    ("g2_d128", 2 * 2 * 150, 2, 6, 3, 128),
+    ("g16_d64", 2 * 2 * 40, 2, 16, 1, 64),
+    ("g3_d128", 2 * 2 * 70, 2, 6, 2, 128),
+    # chunk lengths that are multiples of the 128-key workgroup tile (unmasked full tiles)
+    ("aligned_g4_d128", 2 * 2 * 512, 2, 8, 2, 128),
+    ("aligned_g1_d64", 2 * 4 * 256, 4, 4, 4, 64),
+    ("r16_c256", 2 * 16 * 256, 16, 8, 2, 128),
+]
+
+
+@pytest.mark.parametrize("name,S,R,hq,hkv,d", RAGGED, ids=[r[0] for r in RAGGED])
+def test_ragged_shapes(name, S, R, hq, hkv, d):
+    w = inputs.Workload(name, S, R, hq, hkv, d, backward=True)
+    for r in sorted({0, R - 1}):
+        _check_rank(w, r)
+
+
+def test_packed_documents_small():
+    cu = np.array([0, 1, 2, 130, 131, 300, 301, 520, 767, 768], dtype=np.int32)
+    w = inputs.Workload("packed_small", 768, 4, 8, 2, 128, backward=True, packed=True)
+    for r in range(w.cp):
+        _check_rank(w, r, cu)
+
+
+def test_single_token_chunks():
+    w = inputs.Workload("c1", 4, 2, 4, 2, 64, backward=True)
+    for r in range(2):
+        _check_rank(w, r)
+
+
+@pytest.mark.timeout(600)
+def test_llama3_8b_fwd_bwd_full_size_sampled():
+    """Llama-3-8B shape, rank 0's share of S=256K at CP=16 (local 16K), 16 ring steps
+    forward and backward on the GPU; dQ on sampled rows and each step's dK/dV on
+    sampled keys against the oracle (which sees every row and key they depend on)."""
+    w = inputs.WORKLOADS["llama3_8b_fwdbwd"]
+    rank = 0
+    inp, ring, o, lse, dq, per_step = _run(w, rank)
+    rng = np.random.default_rng(11)
+    c, L = w.chunk, w.local
+    rows = np.unique(np.concatenate([[0, 1, c - 1, c, c + 1, L - 1], rng.integers(0, L, 20)]))
+    blocks = [inp.kv64[s] for s in ring.schedule()]
+    ro, rl, _ = oracle.rank_forward(inp.q64, inp.qpos, blocks, None, w.scale, rows=rows)
+    assert_o_close(o[rows].cpu().numpy(), ro, "O sampled rows")
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, "LSE sampled rows")
+    rdq, _, _ = oracle.rank_backward(inp.q64[rows], inp.qpos[rows], inp.do64[rows], ro, rl, blocks, None, w.scale)
+    assert_o_close(dq[rows].cpu().numpy(), rdq, "dQ sampled rows")
+    # dK/dV of sampled keys need every local row's LSE and delta: take them from the GPU forward
+    lse64 = lse.cpu().numpy().astype(np.float64)
+    delta64 = oracle.delta_rows(inp.do64, o.cpu().numpy())
+    keys = np.unique(np.concatenate([[0, 1, c - 1, c, L - 1], rng.integers(0, L, 12)]))
+    for t in (0, 1, w.cp - 1):
+        src, dk, dv = per_step[t]
+        k64, v64, kpos = inp.kv64[src]
+        vis = oracle.visibility(inp.qpos, kpos[keys])
+        _, rdk, rdv = oracle.attention_backward_partial(inp.q64, k64[keys], v64[keys], inp.do64, lse64, delta64,
+                                                        vis, w.scale)
+        assert_o_close(dk[keys].cpu().numpy(), rdk, f"dK step {t} sampled keys")
+        assert_o_close(dv[keys].cpu().numpy(), rdv, f"dV step {t} sampled keys")

@@ -93,6 +93,7 @@ RAGGED = [
     ("g16_d64", 2 * 4 * 33, 4, 16, 1, 64),
     ("g8_d128", 2 * 2 * 130, 2, 8, 1, 128),
     ("g3_d64", 2 * 2 * 70, 2, 6, 2, 64),
+    ("r16_c256", 2 * 16 * 256, 16, 8, 2, 128),
 ]
 
 
