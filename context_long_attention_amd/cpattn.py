@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libcpattn.so")
+# CPATTN_LIB may name another build of the same library (same ABI), e.g. a debug build.
+LIB_PATH = os.environ.get("CPATTN_LIB") or os.path.join(_PKG, "libcpattn.so")
 
 CP_OK, CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_HIP = 0, -1, -2, -3
 CP_MASK_FULL, CP_MASK_DIAG_CAUSAL, CP_MASK_DOC, CP_MASK_SKIP = 0, 1, 2, 3

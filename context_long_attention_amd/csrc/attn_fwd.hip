@@ -13,14 +13,19 @@
 //    queries on N): each lane then holds one query and 32 of its keys, so the
 //    row max needs a single exchange between the two half-waves and the row
 //    sum needs none until the epilogue.
-//  * K rows are loaded into the MFMA in a permuted order chosen so that the
-//    fp32 score registers, rounded to bf16, are directly the B operand of the
-//    P V product (O^T = V^T P^T); V is stored transposed in LDS so the A
-//    operand of that product is one 16-byte LDS read.
-//  * K/V tiles are double-buffered in LDS with rows padded by 16 bytes (the
-//    MFMA operand reads of 16 lanes then hit distinct banks and every read is
-//    a base register plus an immediate offset); the global loads of tile i+1
-//    are issued before the MFMAs of tile i.
+//  * The P registers, rounded to bf16, are directly the B operand of the P V
+//    product (O^T = V^T P^T).  V stays row-major in LDS; its transposed MFMA
+//    operand comes from the gfx950 transposing LDS read (ds_read_tr16_b64:
+//    16 lanes read a 4-row x 16-column block and each lane receives 4
+//    consecutive rows of one column), two reads per MFMA.
+//  * K/V tiles are fetched with buffer loads (rows past the end of a ragged
+//    tile read as zero through the descriptor's range check), double-buffered
+//    in LDS with rows padded so that every operand read is conflict-free and a
+//    base register plus an immediate offset; the loads of tile i+1 are issued
+//    before the MFMAs of tile i.
+//  * The running maximum is only raised when a row's maximum grows by more
+//    than 2^8 in the exp2 domain, so the accumulator is rescaled rarely; P is
+//    then bounded by 256, which fp32 accumulation and bf16 rounding absorb.
 //  * Tiles with no visible pair are never visited (block-sparse skip); the
 //    element mask is applied only to partially visible or ragged tiles.
 //  * Workgroup ids are mapped so each XCD (ids equal mod 8) works on one
@@ -67,24 +72,13 @@ struct FwdParams {
     int32_t n_work;
 };
 
-// Key (within a 64-key tile) held by score register r of key block kb in half
-// hl of the wave.  MFMA output row m = 8i + 4hl + j (r = 4i + j) is fed by K
-// row perm(m) = 16(i/2) + 8hl + 4(i%2) + j, so that registers 8(s%2)..8(s%2)+7
-// of block s/2 hold keys 16s + 8hl + 0..7: the B operand of PV step s.
+// Key (within a 64-key tile) held by score register r = 4i + j of key block kb
+// in half hl of the wave: the 32x32 MFMA output row 8i + 4hl + j.  Registers
+// 8(s%2)..8(s%2)+7 of block s/2 hold keys 16s + 4hl + {0..3, 8..11}: the B
+// operand of P V step s, matched by two transposing reads of V rows.
 __device__ __forceinline__ int key_of_reg(int kb, int r, int hl) {
-    const int i = r >> 2, j = r & 3;
-    return 32 * kb + 16 * (i >> 1) + 8 * hl + 4 * (i & 1) + j;
+    return 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
 }
-
-__device__ __forceinline__ int perm_row(int m) {
-    const int i = m >> 3, h = (m >> 2) & 1, j = m & 3;
-    return 16 * (i >> 1) + 8 * h + 4 * (i & 1) + j;
-}
-
-// LDS row pitches (bytes): K tile [kBN][D], transposed V tile [D][kBN].
-template <int D>
-constexpr int k_pitch() { return D * 2 + 16; }
-constexpr int kVtPitch = kBN * 2 + 16;
 
 __device__ __forceinline__ int doc_index(const int32_t* cu, int n_docs, int pos) {
     int lo = 0, hi = n_docs - 1;
@@ -124,77 +118,62 @@ __device__ __forceinline__ bool tile_full(int mask, int q0, int lo1, int kpos0, 
     return k1 <= q0 && k0 >= lo1;
 }
 
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// LDS tile layout.  One buffer load per wave moves 1 KiB (64 lanes x 16 B)
+// straight into LDS, lane i landing at base + 16 i; that KiB holds RB = 1024 /
+// (2D) consecutive rows, stored chunk-major: (row j, 16-byte chunk c) at
+// 16 (RB c + j).  Blocks are BLK bytes apart; the padding makes the 16-byte
+// operand reads of 16 consecutive rows and the transposing reads of a 4 x 16
+// block hit distinct banks.
 template <int D>
-struct Stage {
-    u32x4 kreg[D / 32];  // K: BN*D/8 16-byte chunks over 256 threads
-    u32x4 vreg[4];       // V: 4 keys x 8 dims per thread
+struct TileLayout {
+    static constexpr int RB = 1024 / (2 * D);
+    static constexpr int BLK = 1024 + (D == 128 ? 64 : 128);
+    static constexpr int NBLK = kBN / RB;
+    static constexpr int BYTES = NBLK * BLK;
+    // byte offset of element (row, col) of a tile
+    static __device__ __forceinline__ int off(int row, int col) {
+        return (row / RB) * BLK + 16 * (RB * (col / 8) + row % RB) + 2 * (col % 8);
+    }
 };
 
-template <int D>
-__device__ __forceinline__ void load_tile(Stage<D>& st, const uint16_t* __restrict__ kbase,
-                                          const uint16_t* __restrict__ vbase, int64_t row_stride,
-                                          int kcount, int tid) {
-    constexpr int CPR = D / 8;  // 16-byte chunks per key row
-#pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-        const int c = tid + kThreads * j;
-        const int kr = c / CPR, dc = c % CPR;
-        u32x4 val = {0u, 0u, 0u, 0u};
-        if (kr < kcount) val = *reinterpret_cast<const u32x4*>(kbase + kr * row_stride + dc * 8);
-        st.kreg[j] = val;
-    }
-    constexpr int VBLOCKS = (kBN / 4) * (D / 8);
-    if (VBLOCKS == kThreads || tid < VBLOCKS) {
-        const int kq = tid / (D / 8), dg = tid % (D / 8);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int kr = kq * 4 + r;
-            u32x4 val = {0u, 0u, 0u, 0u};
-            if (kr < kcount) val = *reinterpret_cast<const u32x4*>(vbase + kr * row_stride + dg * 8);
-            st.vreg[r] = val;
-        }
-    }
+// Buffer descriptor covering rows [0, rows) of one head of a [rows, H, D] bf16
+// tensor starting at `base`: reads of later rows return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int rows, int row_bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, rows * row_bytes, 0x00020000);
 }
 
+// Issue the direct-to-LDS loads of one 64-row tile (this wave's blocks).
 template <int D>
-__device__ __forceinline__ void store_tile(const Stage<D>& st, char* klds, char* vlds, int tid) {
-    constexpr int CPR = D / 8;
+__device__ __forceinline__ void load_tile_lds(char* dst, __amdgpu_buffer_rsrc_t rs, int row_bytes, int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    using L = TileLayout<D>;
+    const int j = lane % L::RB, c = lane / L::RB;
 #pragma unroll
-    for (int j = 0; j < D / 32; ++j) {
-        const int c = tid + kThreads * j;
-        const int kr = c / CPR, dc = c % CPR;
-        *reinterpret_cast<u32x4*>(klds + kr * k_pitch<D>() + (dc << 4)) = st.kreg[j];
+    for (int b = 0; b < L::NBLK / 4; ++b) {
+        const int blk = wave + 4 * b;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * L::BLK), 16,
+                                                 (blk * L::RB + j) * row_bytes + c * 16, 0, 0, 0);
     }
-    constexpr int VBLOCKS = (kBN / 4) * (D / 8);
-    if (VBLOCKS == kThreads || tid < VBLOCKS) {
-        const int kq = tid / (D / 8), dg = tid % (D / 8);
-        // Transpose the 4 keys x 8 dims block: for each dim, the 4 keys are one 8-byte run of V^T.
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int w = e >> 1;
-            const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-            u32x2 pk;
-            pk.x = __builtin_amdgcn_perm(st.vreg[1][w], st.vreg[0][w], sel);
-            pk.y = __builtin_amdgcn_perm(st.vreg[3][w], st.vreg[2][w], sel);
-            const int d = dg * 8 + e;
-            const int off = d * kVtPitch + (kq << 3);
-            *reinterpret_cast<u32x2*>(vlds + off) = pk;
-        }
-    }
+#endif
 }
 
 template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p) {
+    using L = TileLayout<D>;
     constexpr int WPH = 4 / HPW;      // waves per head
     constexpr int BMQ = 32 * WPH;     // query rows per workgroup tile
     constexpr int DS = D / 16;        // MFMA k-steps over the head dim
     constexpr int DB = D / 32;        // 32-row blocks of O^T
-    constexpr int KBYTES = kBN * k_pitch<D>();
-    constexpr int VBYTES = D * kVtPitch;
-    __shared__ __attribute__((aligned(16))) char smem[2 * (KBYTES + VBYTES)];
+    // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
+    __shared__ __attribute__((aligned(16))) char smem[4 * L::BYTES];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int hl = lane >> 5;
     const int ql = lane & 31;
@@ -213,7 +192,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     const int q0 = tile_pos0, q1 = tile_pos0 + tile_rows - 1;
 
     const int head = hb * HPW + wave / WPH;
-    const int kvh = head / p.group;
+    const int kvh = (hb * HPW) / p.group;  // the workgroup's heads share one KV head (HPW divides G)
     const int row_in_tile = (wave % WPH) * 32 + ql;
     const bool row_valid = row_in_tile < tile_rows;
     const int my_row = tile_row0 + row_in_tile;
@@ -273,57 +252,52 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     f32x16 acc[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
-    float m_run = -INFINITY;
-    float l_run = 0.f;
+    float m2 = -INFINITY;  // reference maximum of the row, in the exp2 domain (scores * c2)
+    float l_run = 0.f;     // this half-wave's share of sum_j exp2(c2 s_j - m2)
     const float c2 = p.scale_log2;
-    const int64_t kv_stride = (int64_t)p.hkv * D;
+    const int row_bytes = p.hkv * D * 2;
 
     auto tile_of = [&](int it, int& s, int& t) {
         s = (it < n0) ? 0 : 1;
         t = s ? rng[1].t_lo + (it - n0) : rng[0].t_lo + it;
     };
-
-    Stage<D> st;
-    if (n_it > 0) {
-        int s, t;
-        tile_of(0, s, t);
-        const int64_t r0 = p.ks_row0[s] + (int64_t)t * kBN;
-        const uint16_t* kb = p.k + (r0 * p.hkv + kvh) * D;
-        const uint16_t* vb = p.v + (r0 * p.hkv + kvh) * D;
-        load_tile<D>(st, kb, vb, kv_stride, min(kBN, p.ks_len[s] - t * kBN), tid);
-        store_tile<D>(st, smem, smem + KBYTES, tid);
-    }
-    __syncthreads();
-
-    for (int it = 0; it < n_it; ++it) {
-        char* klds = smem + (it & 1) * (KBYTES + VBYTES);
-        char* vlds = klds + KBYTES;
+    auto rsrc_of = [&](const uint16_t* tensor, int it) -> __amdgpu_buffer_rsrc_t {
         int s, t;
         tile_of(it, s, t);
-        if (it + 1 < n_it) {
-            int s2, t2;
-            tile_of(it + 1, s2, t2);
-            const int64_t r0 = p.ks_row0[s2] + (int64_t)t2 * kBN;
-            const uint16_t* kb = p.k + (r0 * p.hkv + kvh) * D;
-            const uint16_t* vb = p.v + (r0 * p.hkv + kvh) * D;
-            load_tile<D>(st, kb, vb, kv_stride, min(kBN, p.ks_len[s2] - t2 * kBN), tid);
-        }
+        const int64_t r0 = p.ks_row0[s] + (int64_t)t * kBN;
+        const int rows = min(kBN, p.ks_len[s] - t * kBN);
+        return tile_rsrc(tensor + (r0 * p.hkv + kvh) * D, rows, row_bytes);
+    };
+    char* const kbuf[2] = {smem, smem + L::BYTES};
+    char* const vbuf[2] = {smem + 2 * L::BYTES, smem + 3 * L::BYTES};
 
-        // ---- S^T = K Q^T for 64 keys x 32 queries
-        f32x16 sc[2];
+    // per-lane parts of the operand addresses (see TileLayout and key_of_reg)
+    const int k_lane = L::off(ql, 8 * hl);
+    const int grp = lane >> 4, jl = lane & 15;
+    const int v_lane = L::off(4 * (grp >> 1) + (jl >> 2), 16 * (grp & 1) + 4 * (jl & 3));
+
+    // S^T of one tile: 64 keys x this wave's 32 queries
+    auto scores = [&](const char* kt, f32x16* sc) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             sc[kb] = f32x16{};
-            const int kr = 32 * kb + perm_row(ql);
-            const char* krow = klds + kr * k_pitch<D>() + (hl << 4);
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(krow + (ds << 5));
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + k_lane + L::off(32 * kb, 16 * ds));
                 sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sc[kb], 0, 0, 0);
             }
         }
+    };
 
-        // ---- element mask on partial or ragged tiles
+    // One pipelined step: softmax of tile `it` (scores in cur), the scores of
+    // tile it+1 (into nxt, overlapping the softmax), then O^T += V^T P^T.
+    auto step = [&](int it, f32x16* cur, f32x16* nxt) {
+        if (it + 2 < n_it) load_tile_lds<D>(kbuf[it & 1], rsrc_of(p.k, it + 2), row_bytes, wave, lane);
+        if (it + 1 < n_it) load_tile_lds<D>(vbuf[(it + 1) & 1], rsrc_of(p.v, it + 1), row_bytes, wave, lane);
+        int s, t;
+        tile_of(it, s, t);
+
+        // element mask on partial or ragged tiles
         const int kcount = min(kBN, p.ks_len[s] - t * kBN);
         const int kp0 = p.ks_pos0[s] + t * kBN;
         const int m = mk[s];
@@ -340,22 +314,32 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = key_of_reg(kb, r, hl);
-                    if (key > hi_lim || key < lo_lim) sc[kb][r] = -INFINITY;
+                    if (key > hi_lim || key < lo_lim) cur[kb][r] = -INFINITY;
                 }
         }
 
-        // ---- online softmax (exp2 domain, scale folded into one FMA)
-        float mloc = sc[0][0];
+        // row maximum; the reference maximum is raised only when it grows by more than 2^8
+        float mloc = cur[0][0];
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sc[0][r]);
+        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, cur[0][r]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sc[1][r]);
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, cur[1][r]);
         mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float m_new = fmaxf(m_run, mloc);
-        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * c2);
-        const float nb = -m_use * c2;
-        m_run = m_new;
+        const float mt2 = mloc * c2;
+        const bool raise = mt2 > m2 + 8.f;
+        if (__any(raise)) {
+            const float m2n = raise ? mt2 : m2;
+            const float alpha = (m2n == m2) ? 1.f : __builtin_amdgcn_exp2f(m2 - m2n);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+            m2 = m2n;
+        }
+        const float nb = (m2 == -INFINITY) ? 0.f : -m2;
+
+        // scores of the next tile (its K tile is resident; unused after the last tile)
+        scores(kbuf[(it + 1) & 1], nxt);
+
         float lsum = 0.f;
         bf16x8 pb[4];
 #pragma unroll
@@ -365,35 +349,48 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
                 f32x8 pv;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * half + e], c2, nb));
+                    const float pe = __builtin_amdgcn_exp2f(fmaf(cur[kb][8 * half + e], c2, nb));
                     pv[e] = pe;
                     lsum += pe;
                 }
                 pb[2 * kb + half] = __builtin_convertvector(pv, bf16x8);
             }
         }
-        l_run = l_run * alpha + lsum;
-        if (__any(alpha != 1.f)) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-        }
+        l_run += lsum;
 
-        // ---- O^T += V^T P^T
+        // O^T += V^T P^T: step s4 covers keys 16 s4 + 4hl + {0..3, 8..11}
+        const char* vt = vbuf[it & 1];
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const int d = 32 * db + ql;
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vlds + d * kVtPitch + (s4 << 5) + (hl << 4));
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[s4], acc[db], 0, 0, 0);
+                const char* a0 = vt + v_lane + L::off(16 * s4, 32 * db);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + L::off(8, 0)));
+                const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[s4], acc[db],
+                                                                   0, 0, 0);
             }
         }
+        __syncthreads();  // the loads issued above have landed; buffers of this step are free
+    };
 
-        if (it + 1 < n_it) {
-            char* knext = smem + ((it + 1) & 1) * (KBYTES + VBYTES);
-            store_tile<D>(st, knext, knext + KBYTES, tid);
-        }
+    f32x16 sa[2], sb[2];
+    if (n_it > 0) {
+        // rows past the end of a ragged tile must read as finite values (their P is zero)
+        for (int i = tid; i < 4 * L::BYTES / 16; i += kThreads)
+            *reinterpret_cast<u32x4*>(smem + 16 * i) = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
+        load_tile_lds<D>(kbuf[0], rsrc_of(p.k, 0), row_bytes, wave, lane);
+        load_tile_lds<D>(vbuf[0], rsrc_of(p.v, 0), row_bytes, wave, lane);
+        if (n_it > 1) load_tile_lds<D>(kbuf[1], rsrc_of(p.k, 1), row_bytes, wave, lane);
+        __syncthreads();
+        scores(kbuf[0], sa);
+        __syncthreads();  // every wave has read K(0) before K(2) replaces it
+    }
+    for (int it = 0; it < n_it; it += 2) {
+        step(it, sa, sb);
+        if (it + 1 < n_it) step(it + 1, sb, sa);
     }
 
     // ---- epilogue: normalise, write O (fp32) and LSE (natural log)
@@ -410,7 +407,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
                 *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * hl) = val;
             }
         if (hl == 0) {
-            const float lse = (l_tot > 0.f) ? m_run * p.scale + __logf(l_tot) : -INFINITY;
+            const float lse = (l_tot > 0.f) ? (m2 + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
             p.lse[(int64_t)head * p.q_rows + my_row] = lse;
         }
     }
