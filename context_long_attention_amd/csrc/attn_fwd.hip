@@ -48,8 +48,10 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int kBN = 64;       // keys per tile
-constexpr int kThreads = 256; // 4 waves
+constexpr int kBN = 64;                    // keys per tile
+constexpr int kWaves = kFwdWaves;          // 8 waves: 2 per SIMD, one workgroup per CU
+constexpr int kThreads = 64 * kWaves;
+constexpr int kStages = 4;                 // K/V tiles in flight (LDS ring)
 
 struct FwdParams {
     const uint16_t* q;
@@ -147,15 +149,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, rows * row_bytes, 0x00020000);
 }
 
-// Issue the direct-to-LDS loads of one 64-row tile (this wave's blocks).
+// Issue the direct-to-LDS loads of one 64-row tile (this wave's blocks): every
+// wave issues exactly kLoadsPerTile loads per tile, which the wait counts rely on.
+template <int D>
+constexpr int loads_per_tile() { return TileLayout<D>::NBLK / kWaves; }
+
 template <int D>
 __device__ __forceinline__ void load_tile_lds(char* dst, __amdgpu_buffer_rsrc_t rs, int row_bytes, int wave, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)
     using L = TileLayout<D>;
     const int j = lane % L::RB, c = lane / L::RB;
 #pragma unroll
-    for (int b = 0; b < L::NBLK / 4; ++b) {
-        const int blk = wave + 4 * b;
+    for (int b = 0; b < loads_per_tile<D>(); ++b) {
+        const int blk = wave + kWaves * b;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * L::BLK), 16,
                                                  (blk * L::RB + j) * row_bytes + c * 16, 0, 0, 0);
     }
@@ -165,12 +171,22 @@ __device__ __forceinline__ void load_tile_lds(char* dst, __amdgpu_buffer_rsrc_t 
 template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p) {
     using L = TileLayout<D>;
-    constexpr int WPH = 4 / HPW;      // waves per head
+    constexpr int WPH = kWaves / HPW; // waves per head
     constexpr int BMQ = 32 * WPH;     // query rows per workgroup tile
     constexpr int DS = D / 16;        // MFMA k-steps over the head dim
     constexpr int DB = D / 32;        // 32-row blocks of O^T
-    // [K buffer 0][K buffer 1][V buffer 0][V buffer 1]
-    __shared__ __attribute__((aligned(16))) char smem[4 * L::BYTES];
+    // A ring of kStages K tiles and kStages V tiles, each its own LDS object,
+    // so the compiler can tell that loads in flight into one buffer do not
+    // alias the operand reads of another.
+    __shared__ __attribute__((aligned(16))) char kb0[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char kb1[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char kb2[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char kb3[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char vb0[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char vb1[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char vb2[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char vb3[L::BYTES];
+    static_assert(kStages == 4, "the unrolled ring below assumes four stages");
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -257,19 +273,36 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     const float c2 = p.scale_log2;
     const int row_bytes = p.hkv * D * 2;
 
-    auto tile_of = [&](int it, int& s, int& t) {
-        s = (it < n0) ? 0 : 1;
-        t = s ? rng[1].t_lo + (it - n0) : rng[0].t_lo + it;
+    // Per-segment values held in scalars for the whole tile loop (a runtime
+    // index into the parameter block would reload it from memory every tile).
+    const int len0 = p.ks_len[0], len1 = p.ks_len[1];
+    const int pos0 = p.ks_pos0[0], pos1 = p.ks_pos0[1];
+    const int mk0 = mk[0], mk1 = mk[1];
+    const int tlo0 = rng[0].t_lo, tlo1 = rng[1].t_lo;
+    const int64_t head_off = (int64_t)kvh * D;
+    const uint16_t* const kseg0 = p.k + (int64_t)p.ks_row0[0] * p.hkv * D + head_off;
+    const uint16_t* const kseg1 = p.k + (int64_t)p.ks_row0[1] * p.hkv * D + head_off;
+    const uint16_t* const vseg0 = p.v + (int64_t)p.ks_row0[0] * p.hkv * D + head_off;
+    const uint16_t* const vseg1 = p.v + (int64_t)p.ks_row0[1] * p.hkv * D + head_off;
+    const int64_t tile_elems = (int64_t)kBN * p.hkv * D;
+
+    struct TileRef {
+        int t, len, pos, mask, seg;
     };
-    auto rsrc_of = [&](const uint16_t* tensor, int it) -> __amdgpu_buffer_rsrc_t {
-        int s, t;
-        tile_of(it, s, t);
-        const int64_t r0 = p.ks_row0[s] + (int64_t)t * kBN;
-        const int rows = min(kBN, p.ks_len[s] - t * kBN);
-        return tile_rsrc(tensor + (r0 * p.hkv + kvh) * D, rows, row_bytes);
+    auto tile_of = [&](int it) -> TileRef {
+        const bool second = it >= n0;
+        const int t = second ? tlo1 + (it - n0) : tlo0 + it;
+        return TileRef{t, second ? len1 : len0, second ? pos1 : pos0, second ? mk1 : mk0, second ? 1 : 0};
     };
-    char* const kbuf[2] = {smem, smem + L::BYTES};
-    char* const vbuf[2] = {smem + 2 * L::BYTES, smem + 3 * L::BYTES};
+    // Descriptor of tile `it`; past the last tile an empty descriptor, whose
+    // loads fetch nothing and write zeros (every step issues the same loads).
+    auto rsrc_of = [&](bool is_v, int it) -> __amdgpu_buffer_rsrc_t {
+        const TileRef tr = tile_of(it);
+        const bool live = it < n_it;
+        const uint16_t* base = is_v ? (tr.seg ? vseg1 : vseg0) : (tr.seg ? kseg1 : kseg0);
+        return tile_rsrc(live ? base + tr.t * tile_elems : base, live ? min(kBN, tr.len - tr.t * kBN) : 0,
+                         row_bytes);
+    };
 
     // per-lane parts of the operand addresses (see TileLayout and key_of_reg)
     const int k_lane = L::off(ql, 8 * hl);
@@ -289,108 +322,131 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         }
     };
 
-    // One pipelined step: softmax of tile `it` (scores in cur), the scores of
-    // tile it+1 (into nxt, overlapping the softmax), then O^T += V^T P^T.
-    auto step = [&](int it, f32x16* cur, f32x16* nxt) {
-        if (it + 2 < n_it) load_tile_lds<D>(kbuf[it & 1], rsrc_of(p.k, it + 2), row_bytes, wave, lane);
-        if (it + 1 < n_it) load_tile_lds<D>(vbuf[(it + 1) & 1], rsrc_of(p.v, it + 1), row_bytes, wave, lane);
-        int s, t;
-        tile_of(it, s, t);
+    // Wait until at most `pending` of this wave's loads are in flight (and
+    // every LDS read has completed), then synchronise the workgroup.
+    constexpr int kPending = 2 * 2 * loads_per_tile<D>();  // the loads of the last two steps
+    auto ring_barrier = [&]() {
+        // s_waitcnt: vmcnt = kPending (bits 3:0 and 15:14), expcnt 7 (no wait), lgkmcnt 0
+        __builtin_amdgcn_s_waitcnt((kPending & 15) | ((kPending >> 4) << 14) | (7 << 4));
+        __builtin_amdgcn_s_barrier();
+    };
 
-        // element mask on partial or ragged tiles
-        const int kcount = min(kBN, p.ks_len[s] - t * kBN);
-        const int kp0 = p.ks_pos0[s] + t * kBN;
-        const int m = mk[s];
-        const bool full = tile_full(m, q0, m == CP_MASK_DOC ? lo1 : 0, p.ks_pos0[s], p.ks_len[s], t);
-        if (!full || kcount < kBN) {
-            int hi_lim = kcount - 1;
-            int lo_lim = -kBN;
-            if (m != CP_MASK_FULL) {
-                hi_lim = min(hi_lim, my_pos - kp0);
-                if (m == CP_MASK_DOC) lo_lim = my_lo - kp0;
-            }
+    bf16x8 pb[4];  // P of the previous tile (bf16), consumed by the next step's P V
+    // Rotated pipeline step `it` (0 <= it <= n_it):
+    //   loads:  K(it+4) into the K slot freed by K(it), V(it+2) into the V slot freed by V(it-2);
+    //   PV:     O^T += V(it-1)^T P(it-1)                       (MFMA, overlaps the next part)
+    //   mask, row max and rare rescale of tile it's scores  (VALU)
+    //   scores of tile it+1 (MFMA) overlapping exp / sum / bf16 of tile it (VALU) -> P(it)
+    // Slots: K(j) and V(j) live in slot j mod 4, so each unrolled copy below
+    // touches statically known buffers.
+    auto step = [&](int it, f32x16* cur, f32x16* nxt, char* k_fill, const char* k_read, char* v_fill,
+                    const char* v_read) {
+        load_tile_lds<D>(k_fill, rsrc_of(false, it + 4), row_bytes, wave, lane);
+        load_tile_lds<D>(v_fill, rsrc_of(true, it + 2), row_bytes, wave, lane);
+
+        if (it >= 1) {
+            // O^T += V^T P^T: step s4 covers keys 16 s4 + 4hl + {0..3, 8..11}
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int s4 = 0; s4 < 4; ++s4) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = key_of_reg(kb, r, hl);
-                    if (key > hi_lim || key < lo_lim) cur[kb][r] = -INFINITY;
+                for (int db = 0; db < DB; ++db) {
+                    const char* a0 = v_read + v_lane + L::off(16 * s4, 32 * db);
+                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + L::off(8, 0)));
+                    const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[s4],
+                                                                       acc[db], 0, 0, 0);
                 }
+            }
         }
 
-        // row maximum; the reference maximum is raised only when it grows by more than 2^8
-        float mloc = cur[0][0];
-#pragma unroll
-        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, cur[0][r]);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, cur[1][r]);
-        mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-        const float mt2 = mloc * c2;
-        const bool raise = mt2 > m2 + 8.f;
-        if (__any(raise)) {
-            const float m2n = raise ? mt2 : m2;
-            const float alpha = (m2n == m2) ? 1.f : __builtin_amdgcn_exp2f(m2 - m2n);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-            m2 = m2n;
-        }
-        const float nb = (m2 == -INFINITY) ? 0.f : -m2;
-
-        // scores of the next tile (its K tile is resident; unused after the last tile)
-        scores(kbuf[(it + 1) & 1], nxt);
-
-        float lsum = 0.f;
-        bf16x8 pb[4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                f32x8 pv;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float pe = __builtin_amdgcn_exp2f(fmaf(cur[kb][8 * half + e], c2, nb));
-                    pv[e] = pe;
-                    lsum += pe;
+        if (it < n_it) {
+            const TileRef tr = tile_of(it);
+            // element mask on partial or ragged tiles: key k of the tile is visible
+            // iff lo_lim <= k <= hi_lim, tested as one unsigned range compare with the
+            // lane's 4 hl folded into the limits
+            const int kcount = min(kBN, tr.len - tr.t * kBN);
+            const int kp0 = tr.pos + tr.t * kBN;
+            const int m = tr.mask;
+            const bool full = tile_full(m, q0, m == CP_MASK_DOC ? lo1 : 0, tr.pos, tr.len, tr.t);
+            if (!full || kcount < kBN) {
+                int hi_lim = kcount - 1;
+                int lo_lim = 0;
+                if (m != CP_MASK_FULL) {
+                    hi_lim = min(hi_lim, my_pos - kp0);
+                    if (m == CP_MASK_DOC) lo_lim = max(0, my_lo - kp0);
                 }
-                pb[2 * kb + half] = __builtin_convertvector(pv, bf16x8);
+                const int lo_l = lo_lim - 4 * hl;
+                const unsigned span = (unsigned)(hi_lim - lo_lim);
+                const bool none = hi_lim < lo_lim;
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) {
+                        const int key0 = key_of_reg(kb, r, 0);
+                        if (none || (unsigned)(key0 - lo_l) > span) cur[kb][r] = -INFINITY;
+                    }
             }
-        }
-        l_run += lsum;
 
-        // O^T += V^T P^T: step s4 covers keys 16 s4 + 4hl + {0..3, 8..11}
-        const char* vt = vbuf[it & 1];
+            // row maximum; the reference maximum is raised only when it grows by more than 2^8
+            float mloc = cur[0][0];
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
+            for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, cur[0][r]);
 #pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const char* a0 = vt + v_lane + L::off(16 * s4, 32 * db);
-                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + L::off(8, 0)));
-                const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[s4], acc[db],
-                                                                   0, 0, 0);
+            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, cur[1][r]);
+            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+            const float mt2 = mloc * c2;
+            const bool raise = mt2 > m2 + 8.f;
+            if (__any(raise)) {
+                const float m2n = raise ? mt2 : m2;
+                const float alpha = (m2n == m2) ? 1.f : __builtin_amdgcn_exp2f(m2 - m2n);
+                l_run *= alpha;
+#pragma unroll
+                for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+                m2 = m2n;
             }
+            const float nb = (m2 == -INFINITY) ? 0.f : -m2;
+
+            // scores of the next tile (its K tile is resident; unused after the last tile)
+            scores(k_read, nxt);
+
+            float part[4];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    f32x8 pv;
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        pv[e] = __builtin_amdgcn_exp2f(fmaf(cur[kb][8 * half + e], c2, nb));
+                    pb[2 * kb + half] = __builtin_convertvector(pv, bf16x8);
+                    part[2 * kb + half] =
+                        ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+                }
+            }
+            l_run += (part[0] + part[1]) + (part[2] + part[3]);
         }
-        __syncthreads();  // the loads issued above have landed; buffers of this step are free
+        ring_barrier();  // the tiles the next step reads have landed; this step's slots are free
     };
 
     f32x16 sa[2], sb[2];
     if (n_it > 0) {
-        // rows past the end of a ragged tile must read as finite values (their P is zero)
-        for (int i = tid; i < 4 * L::BYTES / 16; i += kThreads)
-            *reinterpret_cast<u32x4*>(smem + 16 * i) = u32x4{0u, 0u, 0u, 0u};
+        load_tile_lds<D>(kb0, rsrc_of(false, 0), row_bytes, wave, lane);
+        load_tile_lds<D>(kb1, rsrc_of(false, 1), row_bytes, wave, lane);
         __syncthreads();
-        load_tile_lds<D>(kbuf[0], rsrc_of(p.k, 0), row_bytes, wave, lane);
-        load_tile_lds<D>(vbuf[0], rsrc_of(p.v, 0), row_bytes, wave, lane);
-        if (n_it > 1) load_tile_lds<D>(kbuf[1], rsrc_of(p.k, 1), row_bytes, wave, lane);
-        __syncthreads();
-        scores(kbuf[0], sa);
-        __syncthreads();  // every wave has read K(0) before K(2) replaces it
-    }
-    for (int it = 0; it < n_it; it += 2) {
-        step(it, sa, sb);
-        if (it + 1 < n_it) step(it + 1, sb, sa);
+        scores(kb0, sa);
+        // issue order matters for the wait counts: V0, K2, V1, K3, then two per step
+        load_tile_lds<D>(vb0, rsrc_of(true, 0), row_bytes, wave, lane);
+        load_tile_lds<D>(kb2, rsrc_of(false, 2), row_bytes, wave, lane);
+        load_tile_lds<D>(vb1, rsrc_of(true, 1), row_bytes, wave, lane);
+        load_tile_lds<D>(kb3, rsrc_of(false, 3), row_bytes, wave, lane);
+        ring_barrier();  // K(1) and V(0) have landed; every wave has read K(0)
+        for (int it = 0; it <= n_it; it += 4) {
+            step(it, sa, sb, kb0, kb1, vb2, vb3);
+            if (it + 1 <= n_it) step(it + 1, sb, sa, kb1, kb2, vb3, vb0);
+            if (it + 2 <= n_it) step(it + 2, sa, sb, kb2, kb3, vb0, vb1);
+            if (it + 3 <= n_it) step(it + 3, sb, sa, kb3, kb0, vb1, vb2);
+        }
     }
 
     // ---- epilogue: normalise, write O (fp32) and LSE (natural log)

@@ -27,7 +27,7 @@ cp_status fail(cp_status s, const std::string& msg) {
 TileGeom fwd_geom(int hq, int hkv) {
     int g = hq / hkv;
     int hpw = (g % 4 == 0) ? 4 : (g % 2 == 0 ? 2 : 1);
-    return TileGeom{128 / hpw, 64, hpw};
+    return TileGeom{32 * kFwdWaves / hpw, 64, hpw};
 }
 
 int64_t doc_start_host(const int32_t* cu, int32_t n_docs, int64_t pos) {

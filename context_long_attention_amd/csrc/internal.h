@@ -9,9 +9,11 @@
 
 namespace cpattn {
 
-// Forward tile geometry.  A workgroup is 4 wave64s; each wave owns 32 query
-// rows of one head.  hpw heads of one GQA group share a workgroup (and every
-// K/V tile it stages), so a workgroup covers bm = 128 / hpw query rows.
+// Forward tile geometry.  A workgroup is kFwdWaves wave64s; each wave owns 32
+// query rows of one head.  hpw heads of one GQA group share a workgroup (and
+// every K/V tile it stages), so a workgroup covers bm = 32 * kFwdWaves / hpw
+// query rows.
+constexpr int kFwdWaves = 8;
 struct TileGeom {
     int bm;   // query rows per workgroup tile
     int bn;   // keys per K/V tile
