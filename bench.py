@@ -109,15 +109,77 @@ def cpu_baseline(w, rank, heads):
             "seconds": dt, "flops": flops}
 
 
+def measure(torch, w, rank, steps, warmup, backward):
+    """Time `steps` whole-rank passes (forward ring, plus the backward ring if asked)."""
+    from context_long_attention_amd.ring import RankRing
+    t0 = time.perf_counter()
+    q, kv = make_rank_inputs(torch, w, rank)
+    d_o = None
+    if backward:
+        from context_long_attention_amd import cpattn, inputs
+        c = w.chunk
+        pos = cpattn.cp_partition_zigzag(w.seq_len, w.cp, rank)
+        d_o = _dev_bf16(torch, inputs.chunks_normal(inputs.SEED_DO, [int(pos[0]) // c, int(pos[c]) // c], c,
+                                                    w.hq, w.dim))
+    torch.cuda.synchronize()
+    log(f"{w.name}: inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
+    ring = RankRing(w, rank)
+    pairs = sum(ring.step_pairs(t) for t in range(w.cp))
+    flops_fwd = pairs * w.hq * w.dim * 4
+    flops_bwd = pairs * w.hq * w.dim * 10
+    fwd_timer = KernelTimer(torch, "fwd")
+    bwd_timer = KernelTimer(torch, "bwd")
+    kv_of = kv.__getitem__
+
+    def timer(step, what, stream):
+        fwd_timer(step, what, stream)
+        bwd_timer(step, what, stream)
+
+    def one_step():
+        # the host part of the path (partition, per-step classes) is redone every step
+        r = RankRing(w, rank)
+        o, lse, _ = r.forward(q, kv_of, stage=True, timer=timer)
+        if backward:
+            r.backward(q, d_o, o, lse, kv_of, stage=True, keep_steps=False, timer=timer)
+
+    for i in range(warmup):
+        one_step()
+        torch.cuda.synchronize()
+        log(f"{w.name}: warmup {i + 1}/{warmup} done")
+    fwd_timer.enabled = bwd_timer.enabled = True
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        one_step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    out = {"ms": ms, "fwd_kernel_ms": fwd_timer.total_ms() / steps, "flops_fwd": flops_fwd,
+           "flops_bwd": flops_bwd if backward else 0, "launches": w.cp}
+    if backward:
+        out["bwd_kernel_ms"] = bwd_timer.total_ms() / steps
+    log(f"{w.name}: {steps} steps, {ms:.3f} ms/step, fwd kernels {out['fwd_kernel_ms']:.3f} ms"
+        + (f", bwd kernels {out['bwd_kernel_ms']:.3f} ms" if backward else ""))
+    return out
+
+
+def tflops(flops, ms):
+    return flops / (ms * 1e-3) / 1e12
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_fwd")
+    ap.add_argument("--bwd-workload", default="llama3_8b_fwdbwd")
     ap.add_argument("--rank", type=int, default=0)
     ap.add_argument("--cpu-heads", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bwd", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (one rank's share of the ring); --gpus {args.gpus} "
@@ -126,48 +188,14 @@ def main():
 
     import torch
     from context_long_attention_amd import cpattn, inputs
-    from context_long_attention_amd.ring import RankRing
 
-    w = inputs.WORKLOADS[args.workload]
     cpattn.lib()
     torch.cuda.set_device(0)
+    w = inputs.WORKLOADS[args.workload]
     log(f"workload {w.name}: S={w.seq_len} CP={w.cp} Hq={w.hq} Hkv={w.hkv} D={w.dim} rank={args.rank}")
-    t0 = time.perf_counter()
-    q, kv = make_rank_inputs(torch, w, args.rank)
-    torch.cuda.synchronize()
-    log(f"inputs resident in HBM ({time.perf_counter() - t0:.1f} s)")
-
-    ring = RankRing(w, args.rank)
-    pairs = [ring.step_pairs(t) for t in range(w.cp)]
-    flops_fwd = sum(pairs) * w.hq * w.dim * 4
-    timer = KernelTimer(torch, "fwd")
-    kv_of = kv.__getitem__
-
-    def one_step():
-        # host part of the path: partition and per-step classes are recomputed each step
-        r = RankRing(w, args.rank)
-        return r.forward(q, kv_of, stage=True, timer=timer)
-
-    for i in range(args.warmup):
-        one_step()
-        torch.cuda.synchronize()
-        log(f"warmup {i + 1}/{args.warmup} done")
-    timer.enabled = True
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record()
-    for _ in range(args.steps):
-        one_step()
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    kern_ms = timer.total_ms() / args.steps
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step, fwd kernels {kern_ms:.3f} ms/step")
-
-    value = flops_fwd / (ms * 1e-3) / 1e12
-    achieved = flops_fwd / (kern_ms * 1e-3) / 1e12
-    n_launch = w.cp
+    fwd = measure(torch, w, args.rank, args.steps, args.warmup, backward=False)
+    value = tflops(fwd["flops_fwd"], fwd["ms"])
+    achieved = tflops(fwd["flops_fwd"], fwd["fwd_kernel_ms"])
     record = {
         "metric": "causal attention TFLOP/s per ring-step share (fwd, fwd+bwd); % bf16 MFMA peak",
         "value": round(value, 2),
@@ -175,7 +203,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms, 4),
+        "ms_per_step": round(fwd["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -186,13 +214,26 @@ def main():
                    "ring_steps": w.cp, "pass": "fwd"},
         "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
         "kernel_only": {"tflops": round(achieved, 2), "pct_bf16_peak": round(100 * achieved / BF16_PEAK_TFLOPS, 2),
-                        "ms_per_step": round(kern_ms, 4)},
+                        "ms_per_step": round(fwd["fwd_kernel_ms"], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "kernel": "fwd_step_kernel<128,4>",
-                     "flops_per_launch": flops_fwd / n_launch,
-                     "avg_launch_ms": round(kern_ms / n_launch, 4)},
+                     "flops_per_launch": fwd["flops_fwd"] / fwd["launches"],
+                     "avg_launch_ms": round(fwd["fwd_kernel_ms"] / fwd["launches"], 4)},
     }
+    if not args.no_bwd:
+        wb = inputs.WORKLOADS[args.bwd_workload]
+        fb = measure(torch, wb, args.rank, max(1, args.steps // 2), 1, backward=True)
+        total = fb["flops_fwd"] + fb["flops_bwd"]
+        record["fwd_bwd"] = {
+            "workload": wb.name, "seq_len": wb.seq_len, "cp": wb.cp, "ring_steps": wb.cp,
+            "tflops": round(tflops(total, fb["ms"]), 2),
+            "pct_bf16_peak": round(100 * tflops(total, fb["ms"]) / BF16_PEAK_TFLOPS, 2),
+            "ms_per_step": round(fb["ms"], 4),
+            "fwd_kernel_tflops": round(tflops(fb["flops_fwd"], fb["fwd_kernel_ms"]), 2),
+            "bwd_kernel_tflops": round(tflops(fb["flops_bwd"], fb["bwd_kernel_ms"]), 2),
+            "bwd_kernel_ms_per_step": round(fb["bwd_kernel_ms"], 4),
+        }
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host (cpu_baseline)")
         record["cpu_baseline"] = cpu_baseline(w, args.rank, args.cpu_heads)

@@ -16,16 +16,30 @@ def note(msg: str) -> None:
     print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
 
 
+def _to_device(bits: np.ndarray):
+    import torch
+    return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+
 def device_bf16(x32: np.ndarray):
     """float32 array -> (bf16-rounded float64 copy for the oracle, device bf16 tensor)."""
-    import torch
     bits = inputs.bf16_bits(x32)
-    dev = torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
-    return inputs.bf16_to_f32(bits).astype(np.float64), dev
+    return inputs.bf16_to_f32(bits).astype(np.float64), _to_device(bits)
+
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    return inputs.bf16_to_f32(bits).astype(np.float64)
 
 
 class RankInputs:
-    """Seeded inputs of one rank: local Q/dO and the KV block of every source rank."""
+    """Seeded inputs of one rank: local Q/dO and the KV block of every source rank.
+
+    Host copies are kept as bf16 bit patterns and widened to float64 only when
+    the oracle asks for them (``q64``, ``kv64[s]``, ``blocks``), so the largest
+    workloads fit in host memory.  Sources not listed in ``sources`` get a
+    shared all-zero block on the device (use it only for steps with nothing
+    visible).
+    """
 
     def __init__(self, w: inputs.Workload, rank: int, sources=None, want_do=False):
         import oracle
@@ -34,20 +48,60 @@ class RankInputs:
         R = w.cp
         self.qpos = oracle.zigzag_positions(w.seq_len, R, rank)
         qa, qb = oracle.zigzag_chunks(R, rank)
-        self.q64, self.q = device_bf16(inputs.chunks_normal(inputs.SEED_Q, [qa, qb], c, w.hq, w.dim))
+        self.q_bits = inputs.bf16_bits(inputs.chunks_normal(inputs.SEED_Q, [qa, qb], c, w.hq, w.dim))
+        self.q = _to_device(self.q_bits)
         if want_do:
-            self.do64, self.do = device_bf16(inputs.chunks_normal(inputs.SEED_DO, [qa, qb], c, w.hq, w.dim))
+            self.do_bits = inputs.bf16_bits(inputs.chunks_normal(inputs.SEED_DO, [qa, qb], c, w.hq, w.dim))
+            self.do = _to_device(self.do_bits)
         self.kv = {}
-        self.kv64 = {}
+        self.kv_bits = {}
+        self.kpos = {}
+        self._zero = None
         for s in (range(R) if sources is None else sources):
             ka, kb = oracle.zigzag_chunks(R, s)
-            k64, k = device_bf16(inputs.chunks_normal(inputs.SEED_K, [ka, kb], c, w.hkv, w.dim))
-            v64, v = device_bf16(inputs.chunks_normal(inputs.SEED_V, [ka, kb], c, w.hkv, w.dim))
-            self.kv[s] = (k, v)
-            self.kv64[s] = (k64, v64, oracle.zigzag_positions(w.seq_len, R, s))
+            kbits = inputs.bf16_bits(inputs.chunks_normal(inputs.SEED_K, [ka, kb], c, w.hkv, w.dim))
+            vbits = inputs.bf16_bits(inputs.chunks_normal(inputs.SEED_V, [ka, kb], c, w.hkv, w.dim))
+            self.kv_bits[s] = (kbits, vbits)
+            self.kv[s] = (_to_device(kbits), _to_device(vbits))
+            self.kpos[s] = oracle.zigzag_positions(w.seq_len, R, s)
+
+    @property
+    def q64(self):
+        return widen(self.q_bits)
+
+    @property
+    def do64(self):
+        return widen(self.do_bits)
+
+    @property
+    def kv64(self):
+        return _Widened(self)
+
+    def blocks(self, schedule):
+        """Oracle KV blocks in ring order, widened one at a time (a generator)."""
+        for s in schedule:
+            if s in self.kv_bits:
+                k, v = self.kv_bits[s]
+                yield widen(k), widen(v), self.kpos[s]
 
     def kv_of_source(self, s):
-        return self.kv[s]
+        if s in self.kv:
+            return self.kv[s]
+        if self._zero is None:
+            import torch
+            shape = (self.w.local, self.w.hkv, self.w.dim)
+            z = torch.zeros(shape, dtype=torch.bfloat16, device="cuda")
+            self._zero = (z, z)
+        return self._zero
+
+
+class _Widened:
+    def __init__(self, inp):
+        self.inp = inp
+
+    def __getitem__(self, s):
+        k, v = self.inp.kv_bits[s]
+        return widen(k), widen(v), self.inp.kpos[s]
 
 
 def assert_o_close(got: np.ndarray, ref: np.ndarray, what: str, live=None):
@@ -76,3 +130,10 @@ def assert_lse_close(got: np.ndarray, ref: np.ndarray, what: str):
     worst = float(err.max()) if err.size else 0.0
     assert worst <= LSE_RTOL, f"{what}: LSE rel err {worst:.3e} > {LSE_RTOL}"
     return worst
+
+
+def sampled_rows(local: int, c: int, n_extra: int, seed: int) -> np.ndarray:
+    """Edge rows of both chunks plus uniform random rows."""
+    rng = np.random.default_rng(seed)
+    edge = [0, 1, 2, c - 1, c, c + 1, local - 2, local - 1]
+    return np.unique(np.concatenate([edge, rng.integers(0, local, n_extra)]))

@@ -1,0 +1,129 @@
+"""Full-size GPU parity of the Llama-3-405B-shaped forward and the packed-document
+Llama-3-8B training step (forward and backward), on sampled outputs that the
+oracle computes one by one from every key they depend on."""
+import numpy as np
+import pytest
+
+import oracle
+from context_long_attention_amd import inputs
+from tests.gpu_common import RankInputs, assert_lse_close, assert_o_close, note, sampled_rows, widen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from context_long_attention_amd import cpattn
+    cpattn.lib()
+
+
+@pytest.mark.timeout(900)
+def test_llama3_405b_forward_full_size_sampled():
+    """Hq=128, Hkv=8 (G=16), D=128: rank 0's share of S=1M at CP=16 (local 64K), 16
+    ring steps of 64K-token KV blocks; final O/LSE on sampled rows and one step's
+    partial LSE."""
+    from context_long_attention_amd.ring import RankRing
+    w = inputs.WORKLOADS["llama3_405b_fwd"]
+    note(f"fwd {w.name} full size rank 0")
+    inp = RankInputs(w, 0)
+    ring = RankRing(w, 0)
+    o, lse, steps = ring.forward(inp.q, inp.kv_of_source, keep_steps=False)
+    torch.cuda.synchronize()
+    rows = sampled_rows(w.local, w.chunk, 8, 3)
+    q_rows = widen(inp.q_bits[rows])
+    ro, rl, _ = oracle.rank_forward(q_rows, inp.qpos[rows], inp.blocks(ring.schedule()), None, w.scale)
+    assert_o_close(o[rows].cpu().numpy(), ro, "405B O sampled rows")
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, "405B LSE sampled rows")
+    assert not torch.isnan(o).any().item()
+
+
+def _packed_setup():
+    """Document layout of the packed workload and the visible pairs of every (rank, step)."""
+    from context_long_attention_amd.ring import RankRing
+    w = inputs.WORKLOADS["llama3_8b_packed"]
+    cu = w.cu_seqlens()
+    pairs = np.zeros((w.cp, w.cp), dtype=np.int64)
+    for r in range(w.cp):
+        ring = RankRing(w, r, cu, device="cpu")
+        for t in range(w.cp):
+            pairs[r, t] = ring.step_pairs(t)
+    return w, cu, pairs
+
+
+@pytest.fixture(scope="module")
+def packed():
+    return _packed_setup()
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("which", ["rank0", "max_work"])
+def test_llama3_8b_packed_fwd_bwd_full_size_sampled(packed, which):
+    """S=2M at CP=64 (local 32K), lognormal documents, doc masks with fully masked
+    tiles skipped; forward and backward on the GPU over all 64 ring steps."""
+    from context_long_attention_amd import cpattn
+    from context_long_attention_amd.ring import RankRing
+    w, cu, pairs = packed
+    rank = 0 if which == "rank0" else int(np.argmax(pairs.sum(axis=1)))
+    ring = RankRing(w, rank, cu)
+    sched = ring.schedule()
+    live_steps = [t for t in range(w.cp) if pairs[rank, t] > 0]
+    sources = sorted({sched[t] for t in live_steps})
+    note(f"packed {w.name} rank={rank} live steps={len(live_steps)} pairs={int(pairs[rank].sum())}")
+    inp = RankInputs(w, rank, sources=sources, want_do=True)
+    o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
+    dq, per_step = ring.backward(inp.q, inp.do, o, lse, inp.kv_of_source)
+    torch.cuda.synchronize()
+
+    rows = sampled_rows(w.local, w.chunk, 24, rank + 1)
+    q_rows, do_rows = widen(inp.q_bits[rows]), widen(inp.do_bits[rows])
+    blocks = lambda: inp.blocks([sched[t] for t in live_steps])
+    ro, rl, _ = oracle.rank_forward(q_rows, inp.qpos[rows], blocks(), cu, w.scale)
+    assert_o_close(o[rows].cpu().numpy(), ro, "packed O", np.isfinite(rl).T)
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, "packed LSE")
+    rdq, _, _ = oracle.rank_backward(q_rows, inp.qpos[rows], do_rows, ro, rl, blocks(), cu, w.scale)
+    assert_o_close(dq[rows].cpu().numpy(), rdq, "packed dQ")
+    # dK/dV of sampled keys of the two busiest steps need every local row's LSE and delta
+    lse64 = lse.cpu().numpy().astype(np.float64)
+    delta64 = oracle.delta_rows(inp.do64, o.cpu().numpy())
+    busiest = sorted(live_steps, key=lambda t: -pairs[rank, t])[:2]
+    rng = np.random.default_rng(7)
+    q64, do64 = inp.q64, inp.do64
+    for t in busiest:
+        src, dk, dv = per_step[t]
+        k64, v64, kpos = inp.kv64[src]
+        keys = np.unique(np.concatenate([[0, w.chunk - 1, w.chunk, w.local - 1], rng.integers(0, w.local, 12)]))
+        vis = oracle.visibility(inp.qpos, kpos[keys], cu)
+        _, rdk, rdv = oracle.attention_backward_partial(q64, k64[keys], v64[keys], do64, lse64, delta64, vis,
+                                                        w.scale)
+        assert_o_close(dk[keys].cpu().numpy(), rdk, f"packed dK step {t}")
+        assert_o_close(dv[keys].cpu().numpy(), rdv, f"packed dV step {t}")
+    # steps with nothing visible leave zero gradients for their blocks
+    for t in range(w.cp):
+        if pairs[rank, t] == 0:
+            _, dk, dv = per_step[t]
+            assert torch.all(dk == 0).item() and torch.all(dv == 0).item()
+    # block map the kernel used on the busiest step, against the host rule everywhere and
+    # against the oracle's brute force on sampled query-tile rows
+    t = busiest[0]
+    p = ring.problem(t)
+    nq, nk = cpattn.cp_block_map_size(p)
+    tm = torch.full((nq, nk), 255, dtype=torch.uint8, device="cuda")
+    k, v = inp.kv_of_source(sched[t])
+    o_t = torch.empty_like(o)
+    l_t = torch.empty_like(lse)
+    cpattn.cp_attn_fwd_step(p, inp.q, k, v, o_t, l_t, tile_map=tm)
+    got = tm.cpu().numpy()
+    host = cpattn.cp_block_map(ring.problem(t, host_docs=True))
+    assert np.array_equal(got, host)
+    bm, bn = cpattn.cp_tile_shape(w.hq, w.hkv, w.dim)
+    kseg = [(int(p.kv_seg[j].pos0), int(p.kv_seg[j].len)) for j in range(p.n_kv_seg)]
+    tiles_per_seg = w.chunk // bm
+    for qt in np.unique(np.concatenate([[0, nq - 1], rng.integers(0, nq, 6)])):
+        seg = 0 if qt < tiles_per_seg else 1
+        pos0 = int(p.q_seg[seg].pos0) + (qt - seg * tiles_per_seg) * bm
+        ref = oracle.tile_map([(pos0, bm)], kseg, bm, bn, cu)
+        assert np.array_equal(got[qt:qt + 1], ref), f"tile map row {qt}"
