@@ -6,43 +6,38 @@
 //   P = exp(scale q.k - LSE) on visible pairs,  dS = P (dO.v - delta),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i += scale sum_j dS_ij k_j.
 //
-// Design (wave64, 32x32x16 bf16 MFMA, fp32 accumulation):
-//  * A workgroup owns 128 keys (32 per wave) of one KV head and walks every
-//    (query head of the GQA group, 32-row query tile) that can see them, so
-//    dK and dV accumulate in registers and are written once, without atomics.
-//  * S = Q K^T and dP = dO V^T put queries on the MFMA M axis; the query rows
-//    are fed in a permuted order so that the P and dS registers are directly
-//    the B operands of dV^T = dO^T P and dK^T = Q^T dS.  The transposed dO and
-//    Q operands come from row-major LDS tiles through the gfx950 transposing
-//    LDS read (ds_read_tr16_b64): 16 lanes read a 4-row x 16-column block and
-//    each lane receives 4 consecutive rows of one column.
-//  * dS goes through LDS once per tile; each wave then computes one 32-column
-//    block of dQ over all 128 keys and adds it to the fp32 accumulator with
-//    hardware float atomics (one add per element per workgroup and tile).
-//  * Query tiles and their LSE/delta rows are double-buffered in LDS; one
-//    barrier per tile.
+// Two kernels, neither with atomics (wave64, 32x32x16 bf16 MFMA, fp32 accumulation):
+//  * bwd_dkdv_kernel: a 4-wave workgroup owns 128 keys (32 per wave) of one KV
+//    head, holds their K and V rows in registers, and walks every (query head of
+//    the group, 32-row query tile) that can see them.  Query and dO tiles, with
+//    their LSE and delta rows, stream HBM -> LDS through a four-slot ring three
+//    tiles ahead.  S = Q K^T and dP = dO V^T put the queries on the MFMA M axis,
+//    so each lane holds one key and its P / dS registers are directly the B
+//    operands of dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T come from the
+//    row-major LDS tiles through the transposing LDS read.  dK/dV stay in
+//    registers and are written once.
+//  * bwd_dq_kernel: the forward kernel's shape (8 waves, 32 query rows of one
+//    head per wave, heads of a GQA group sharing K/V tiles, four-slot ring of
+//    K/V tiles): S^T = K Q^T and dP^T = V dO^T put one query per lane, so the
+//    row's LSE and delta are per-lane scalars, and dQ^T += K^T dS^T reads K
+//    transposed from the same LDS tile.  Each wave owns its dQ rows and adds
+//    its sum to the accumulator once.
+// This recomputes S and dP in both kernels (7 products instead of 5) in
+// exchange for no atomic traffic and two clean streaming loops.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
 #include "internal.h"
+#include "tiles.h"
 
 namespace cpattn {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
+using namespace dev;
 
-constexpr int kThreads = 256;
-constexpr int BK = kBwdKeysPerWG;  // 128 keys per workgroup
-constexpr int BQ = kBwdQRows;      // 32 query rows per tile
+constexpr float kLog2e = 1.4426950408889634f;
 
 struct BwdParams {
     const uint16_t* q;
@@ -59,145 +54,54 @@ struct BwdParams {
     int32_t hq, hkv, group;
     int32_t q_rows;
     float scale, scale_log2;
-    int32_t nq_seg;
+    int32_t nq_seg, nkv_seg;
     int32_t qs_row0[2], qs_pos0[2], qs_len[2];
     int32_t ks_row0[2], ks_pos0[2], ks_len[2];
     int32_t mask[2][2];
-    int32_t ktiles0, n_ktiles;
-    int32_t n_work;
+    // dK/dV kernel: 128-key tiles
+    int32_t ktiles0, n_ktiles, n_work_kv;
+    // dQ kernel: query tiles of BMQ rows
+    int32_t qtiles0, n_qtiles, n_work_q;
 };
 
-// Query index (within the 32-row tile) of score register r in half hl: MFMA
-// row m = 8i + 4hl + j is fed by query row perm(m) = 16(i/2) + 8hl + 4(i%2) + j,
-// so registers 8s..8s+7 hold queries 16s + 8hl + 0..7.
-__device__ __forceinline__ int q_of_reg(int r, int hl) {
-    const int i = r >> 2, j = r & 3;
-    return 16 * (i >> 1) + 8 * hl + 4 * (i & 1) + j;
-}
-
-__device__ __forceinline__ int perm_row(int m) {
-    const int i = m >> 3, h = (m >> 2) & 1, j = m & 3;
-    return 16 * (i >> 1) + 8 * h + 4 * (i & 1) + j;
-}
-
-__device__ __forceinline__ int doc_index(const int32_t* cu, int n_docs, int pos) {
-    int lo = 0, hi = n_docs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu[mid] <= pos)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-
-// A/B operand of a 32x32x16 MFMA whose 8 k-slots of half hl are rows
-// rbase + 8hl + 0..7 of a row-major LDS matrix X at column cbase + (lane % 32):
-// two transposing reads, each giving 4 consecutive rows of one column.
-__device__ __forceinline__ bf16x8 tr_operand(const char* x, int pitch, int rbase, int cbase, int lane) {
-    const int grp = lane >> 4, j = lane & 15;
-    const int row = rbase + 8 * (grp >> 1) + (j >> 2);
-    const int col = cbase + 16 * (grp & 1) + 4 * (j & 3);
-    const char* a0 = x + row * pitch + col * 2;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + 4 * pitch));
-    const s16x8 v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-    return __builtin_bit_cast(bf16x8, v);
-}
+// ============================================================================ dK / dV
+constexpr int kKvWaves = 4;
+constexpr int kKvThreads = 64 * kKvWaves;
+constexpr int BK = kBwdKeysPerWG;  // 128 keys per workgroup
+constexpr int BQ = kBwdQRows;      // 32 query rows per tile
+constexpr int kAuxBytes = 256 * kKvWaves;  // per slot: LSE row, delta row, two dummy areas
 
 template <int D>
-constexpr int row_pitch() { return D * 2 + 16; }
-constexpr int kDsPitch = BQ * 2 + 16;
+constexpr int kv_loads_per_item() { return 2 * (TileLayout<D, BQ>::NBLK / kKvWaves) + 1; }
 
 template <int D>
-struct QStage {
-    u32x4 q[D / 64];   // 32 rows x D/8 chunks over 256 threads
-    u32x4 o[D / 64];
-    float aux;         // lse*log2e, delta or document start of one row
-};
-
-template <int D>
-__device__ __forceinline__ void load_q(QStage<D>& st, const BwdParams& p, int head, int qs, int tq, int mode,
-                                       int tid) {
-    constexpr int CPR = D / 8;
-    const int rows = min(BQ, p.qs_len[qs] - tq * BQ);
-    const int row0 = p.qs_row0[qs] + tq * BQ;
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
-        const int c = tid + kThreads * j;
-        const int r = c / CPR, dc = c % CPR;
-        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-        if (r < rows) {
-            const int64_t off = ((int64_t)(row0 + r) * p.hq + head) * D + dc * 8;
-            a = *reinterpret_cast<const u32x4*>(p.q + off);
-            b = *reinterpret_cast<const u32x4*>(p.d_o + off);
-        }
-        st.q[j] = a;
-        st.o[j] = b;
-    }
-    st.aux = 0.f;
-    if (tid < 3 * BQ) {
-        const int which = tid / BQ, r = tid % BQ;
-        if (which == 0) {
-            float v = INFINITY;  // rows outside the segment: P = 0
-            if (r < rows) {
-                const float l = p.lse[(int64_t)head * p.q_rows + row0 + r];
-                v = (l == -INFINITY) ? INFINITY : l * 1.4426950408889634f;
-            }
-            st.aux = v;
-        } else if (which == 1) {
-            st.aux = (r < rows) ? p.delta[(int64_t)head * p.q_rows + row0 + r] : 0.f;
-        } else if (mode == CP_MASK_DOC && r < rows) {
-            const int pos = p.qs_pos0[qs] + tq * BQ + r;
-            st.aux = __int_as_float(p.cu[doc_index(p.cu, p.n_docs, pos)]);
-        }
-    }
-}
-
-template <int D>
-__device__ __forceinline__ void store_q(const QStage<D>& st, char* qlds, char* olds, float* aux, int tid) {
-    constexpr int CPR = D / 8;
-#pragma unroll
-    for (int j = 0; j < D / 64; ++j) {
-        const int c = tid + kThreads * j;
-        const int r = c / CPR, dc = c % CPR;
-        *reinterpret_cast<u32x4*>(qlds + r * row_pitch<D>() + dc * 16) = st.q[j];
-        *reinterpret_cast<u32x4*>(olds + r * row_pitch<D>() + dc * 16) = st.o[j];
-    }
-    if (tid < 3 * BQ) aux[tid] = st.aux;
-}
-
-struct TileList {
-    int lo[2], hi[2];  // query-tile ranges per query segment
-};
-
-template <int D>
-__global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(const BwdParams p) {
+__global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams p) {
+    using L = TileLayout<D, BQ>;
     constexpr int DS = D / 16;
     constexpr int DB = D / 32;
-    constexpr int RP = row_pitch<D>();
-    constexpr int KT_BYTES = BK * RP;
-    constexpr int QT_BYTES = BQ * RP;
-    constexpr int DS_BYTES = BK * kDsPitch;
-    // [K tile][2 x (Q, dO)][2 x dS^T][2 x aux(3 x 32 floats)]
-    __shared__ __attribute__((aligned(16))) char smem[KT_BYTES + 4 * QT_BYTES + 2 * DS_BYTES + 2 * 3 * BQ * 4];
-    char* ktile = smem;
-    char* qbuf = smem + KT_BYTES;
-    char* dsbuf = qbuf + 4 * QT_BYTES;
-    float* auxbuf = reinterpret_cast<float*>(dsbuf + 2 * DS_BYTES);
+    // four-slot ring: query tile, dO tile and (LSE, delta) rows of one item each
+    __shared__ __attribute__((aligned(16))) char qt0[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char qt1[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char qt2[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char qt3[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char ot0[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char ot1[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char ot2[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char ot3[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char ax0[kAuxBytes];
+    __shared__ __attribute__((aligned(16))) char ax1[kAuxBytes];
+    __shared__ __attribute__((aligned(16))) char ax2[kAuxBytes];
+    __shared__ __attribute__((aligned(16))) char ax3[kAuxBytes];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int hl = lane >> 5;
     const int ql = lane & 31;
 
     const int per_xcd = gridDim.x >> 3;
     const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
-    if (w >= p.n_work) return;
+    if (w >= p.n_work_kv) return;
     const int g = w / p.n_ktiles;
     const int kt = w % p.n_ktiles;
     const int s = (kt < p.ktiles0) ? 0 : 1;
@@ -226,62 +130,72 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(const BwdParams p
             vf[ds] = __builtin_bit_cast(bf16x8, b);
         }
     }
-    // ---- the whole K tile, row-major in LDS, for the dQ product
-    {
-        constexpr int CPR = D / 8;
-        for (int c = tid; c < BK * CPR; c += kThreads) {
-            const int r = c / CPR, dc = c % CPR;
-            u32x4 a = {0u, 0u, 0u, 0u};
-            if (r < kcount) a = *reinterpret_cast<const u32x4*>(p.k + (int64_t)(key_row0 + r) * kv_stride +
-                                                                (int64_t)g * D + dc * 8);
-            *reinterpret_cast<u32x4*>(ktile + r * RP + dc * 16) = a;
+
+    // ---- document ends: (query q, key k) is visible iff k <= q < end of k's document
+    bool any_doc = false;
+    for (int qs = 0; qs < p.nq_seg; ++qs) any_doc |= (p.mask[qs][s] == CP_MASK_DOC);
+    int kend_lane = 0x7fffffff, kend_first = 0x7fffffff, kend_last = 0x7fffffff;
+    if (any_doc) {
+        kend_first = p.cu[doc_index(p.cu, p.n_docs, k0p) + 1];
+        kend_last = p.cu[doc_index(p.cu, p.n_docs, k1p) + 1];
+        int j = doc_index(p.cu, p.n_docs, k0p);
+        if (key_valid) {
+            while (j + 1 < p.n_docs && p.cu[j + 1] <= kp) ++j;
         }
+        kend_lane = p.cu[j + 1];
     }
 
-    // ---- query tiles that see any key of [k0p, k1p], per query segment
-    TileList tl;
-    int docend = 0x7fffffff;
-    bool any_doc = false;
+    // ---- query tiles (per query segment) that see any key of [k0p, k1p]
+    int tlo[2] = {0, 0}, thi[2] = {0, 0};
 #pragma unroll
     for (int qs = 0; qs < 2; ++qs) {
-        tl.lo[qs] = tl.hi[qs] = 0;
         if (qs >= p.nq_seg) continue;
         const int m = p.mask[qs][s];
         const int plen = p.qs_len[qs], ppos = p.qs_pos0[qs];
         const int nqt = (plen + BQ - 1) / BQ;
         if (m == CP_MASK_SKIP || plen == 0 || kcount <= 0) continue;
         if (m == CP_MASK_FULL) {
-            tl.hi[qs] = nqt;
+            thi[qs] = nqt;
             continue;
         }
-        // causal: rows q >= k0p
-        if (k0p > ppos + plen - 1) continue;
-        int lo = (k0p <= ppos) ? 0 : (k0p - ppos) / BQ;
+        if (k0p > ppos + plen - 1) continue;  // causal: rows q >= k0p
+        const int lo = (k0p <= ppos) ? 0 : (k0p - ppos) / BQ;
         int hi = nqt;
-        if (m == CP_MASK_DOC) {
-            any_doc = true;
-            // rows whose document starts at or before k1p: q < end of k1p's document
-            const int d1 = doc_index(p.cu, p.n_docs, k1p);
-            docend = p.cu[d1 + 1];
-            const int qmax = docend - 1;
+        if (m == CP_MASK_DOC) {  // and q < end of the last key's document
+            const int qmax = kend_last - 1;
             hi = (qmax < ppos) ? 0 : min(nqt, (qmax - ppos) / BQ + 1);
         }
         if (lo < hi) {
-            tl.lo[qs] = lo;
-            tl.hi[qs] = hi;
+            tlo[qs] = lo;
+            thi[qs] = hi;
         }
     }
-    (void)any_doc;
-    (void)docend;
-    const int n0 = tl.hi[0] - tl.lo[0];
-    const int per_head = n0 + (tl.hi[1] - tl.lo[1]);
+    const int n0 = thi[0] - tlo[0];
+    const int per_head = n0 + (thi[1] - tlo[1]);
     const int n_it = per_head * p.group;
+    const int qrow_bytes = p.hq * D * 2;
 
-    auto item = [&](int it, int& head, int& qs, int& tq) {
-        head = g * p.group + it / per_head;
-        const int rem = it % per_head;
-        qs = (rem < n0) ? 0 : 1;
-        tq = qs ? tl.lo[1] + (rem - n0) : tl.lo[0] + rem;
+    struct Item {
+        int head, qs, tq;
+    };
+    auto item_of = [&](int it) -> Item {
+        const int head = g * p.group + it / max(per_head, 1);
+        const int rem = it - (head - g * p.group) * per_head;
+        const int qs = (rem < n0) ? 0 : 1;
+        return Item{head, qs, qs ? tlo[1] + (rem - n0) : tlo[0] + rem};
+    };
+    // loads of item `it` (empty descriptors past the end keep every step's load count equal)
+    auto issue = [&](int it, char* qdst, char* odst, char* adst) {
+        const Item x = item_of(it);
+        const bool live = it < n_it;
+        const int rows = live ? min(BQ, p.qs_len[x.qs] - x.tq * BQ) : 0;
+        const int row0 = p.qs_row0[x.qs] + x.tq * BQ;
+        const int64_t off = ((int64_t)row0 * p.hq + x.head) * D;
+        load_tile_lds<D, BQ, kKvWaves>(qdst, tile_rsrc(p.q + off, rows, qrow_bytes), qrow_bytes, wave, lane);
+        load_tile_lds<D, BQ, kKvWaves>(odst, tile_rsrc(p.d_o + off, rows, qrow_bytes), qrow_bytes, wave, lane);
+        const int64_t roff = (int64_t)x.head * p.q_rows + row0;
+        const float* src = (wave == 0) ? p.lse + roff : p.delta + roff;
+        load_dwords_lds(adst + 256 * wave, tile_rsrc(src, wave < 2 ? rows : 0, 4), lane * 4);
     };
 
     f32x16 dka[DB], dva[DB];
@@ -291,144 +205,98 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(const BwdParams p
         dva[db] = f32x16{};
     }
     const float c2 = p.scale_log2;
+    const int q_lane = TileLayout<D, BQ>::off(ql, 8 * hl);
+    const int grp = lane >> 4, jl = lane & 15;
+    const int t_lane = TileLayout<D, BQ>::off(4 * (grp >> 1) + (jl >> 2), 16 * (grp & 1) + 4 * (jl & 3));
+    constexpr int kPending = 2 * kv_loads_per_item<D>();
 
-    QStage<D> st;
-    if (n_it > 0) {
-        int head, qs, tq;
-        item(0, head, qs, tq);
-        load_q<D>(st, p, head, qs, tq, p.mask[qs][s], tid);
-        store_q<D>(st, qbuf, qbuf + QT_BYTES, auxbuf, tid);
-    }
-    __syncthreads();
+    auto step = [&](int it, const char* qsl, const char* osl, const char* asl, char* qfill, char* ofill,
+                    char* afill) {
+        issue(it + 3, qfill, ofill, afill);
+        const Item x = item_of(it);
+        const int m = p.mask[x.qs][s];
+        const int qrows = min(BQ, p.qs_len[x.qs] - x.tq * BQ);
+        const int qpos0 = p.qs_pos0[x.qs] + x.tq * BQ;
 
-    // dQ work split: D/32 column blocks over 4 waves; waves sharing a block split the keys
-    constexpr int WPB = 4 / DB;          // waves per dQ column block
-    const int dq_blk = wave % DB;
-    const int dq_part = wave / DB;
-    constexpr int KSTEPS = (BK / 16) / WPB;
-
-    for (int it = 0; it < n_it; ++it) {
-        const int buf = it & 1;
-        char* qlds = qbuf + buf * 2 * QT_BYTES;
-        char* olds = qlds + QT_BYTES;
-        const float* aux = auxbuf + buf * 3 * BQ;
-        char* dst = dsbuf + buf * DS_BYTES;
-        int head, qs, tq;
-        item(it, head, qs, tq);
-        const int m = p.mask[qs][s];
-        const int qrows = min(BQ, p.qs_len[qs] - tq * BQ);
-        const int qrow0 = p.qs_row0[qs] + tq * BQ;
-        const int qpos0 = p.qs_pos0[qs] + tq * BQ;
-        if (it + 1 < n_it) {
-            int h2, qs2, tq2;
-            item(it + 1, h2, qs2, tq2);
-            load_q<D>(st, p, h2, qs2, tq2, p.mask[qs2][s], tid);
-        }
-
-        // ---- S = Q K^T and dP = dO V^T (32 queries x this wave's 32 keys)
+        // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys
         f32x16 sc = f32x16{}, dp = f32x16{};
-        {
-            const char* qrow = qlds + perm_row(ql) * RP + 16 * hl;
-            const char* orow = olds + perm_row(ql) * RP + 16 * hl;
 #pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(qrow + 32 * ds);
-                sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ds], sc, 0, 0, 0);
-            }
+        for (int ds = 0; ds < DS; ++ds) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(qsl + q_lane + L::off(0, 16 * ds));
+            sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, kf[ds], sc, 0, 0, 0);
+        }
 #pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
-                const bf16x8 a = *reinterpret_cast<const bf16x8*>(orow + 32 * ds);
-                dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ds], dp, 0, 0, 0);
-            }
+        for (int ds = 0; ds < DS; ++ds) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(osl + q_lane + L::off(0, 16 * ds));
+            dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ds], dp, 0, 0, 0);
         }
 
-        // ---- P and dS (fp32), element mask on partially visible or ragged tiles
-        const int q_last = qpos0 + qrows - 1;
-        bool full = (m == CP_MASK_FULL);
-        if (!full) {
-            const int lo_last = (m == CP_MASK_DOC) ? __float_as_int(aux[2 * BQ + qrows - 1]) : 0;
-            full = (k1p <= qpos0) && (lo_last <= k0p);
-        }
-        const bool need_mask = !full || kcount < BK;
+        // P = exp2(c2 s - log2e LSE) and dS = P (dP - delta); rows past a ragged tile
+        // have zero Q and dO and contribute nothing, so only visibility is masked
+        const bool full = (m == CP_MASK_FULL) || (k1p <= qpos0 && qpos0 + qrows - 1 < kend_first);
+        const int qk = qpos0 - kp + 4 * hl;                              // q - k without the register's offset
+        const unsigned span = (unsigned)((m == CP_MASK_DOC ? kend_lane : 0x7fffffff) - kp);
+        const float* lse_row = reinterpret_cast<const float*>(asl);
+        const float* del_row = reinterpret_cast<const float*>(asl + 256);
         f32x16 pr, dsr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int qi = 16 * (i >> 1) + 8 * hl + 4 * (i & 1);
-            const f32x4 l2 = *reinterpret_cast<const f32x4*>(aux + qi);
-            const f32x4 dl = *reinterpret_cast<const f32x4*>(aux + BQ + qi);
-            f32x4 lo4 = {0.f, 0.f, 0.f, 0.f};
-            if (need_mask && m == CP_MASK_DOC) lo4 = *reinterpret_cast<const f32x4*>(aux + 2 * BQ + qi);
+            const int q4 = 8 * i + 4 * hl;
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_row + q4);
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_row + q4);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 4 * i + j;
-                float pv = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -l2[j]));
-                if (need_mask) {
-                    bool vis = key_valid;
-                    if (m != CP_MASK_FULL) {
-                        vis = vis && (kp <= qpos0 + qi + j);
-                        if (m == CP_MASK_DOC) vis = vis && (kp >= __float_as_int(lo4[j]));
-                    }
-                    if (!vis) pv = 0.f;
-                }
+                float pv = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -l4[j] * kLog2e));
+                if (!full && (unsigned)(qk + 8 * i + j) >= span) pv = 0.f;
                 pr[r] = pv;
-                dsr[r] = pv * (dp[r] - dl[j]);
+                dsr[r] = pv * (dp[r] - d4[j]);
             }
         }
-        (void)q_last;
-        bf16x8 pb[2], db8[2];
+        bf16x8 pb[2], sb[2];
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
+        for (int h2 = 0; h2 < 2; ++h2) {
             f32x8 a, b;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                a[e] = pr[8 * s2 + e];
-                b[e] = dsr[8 * s2 + e];
+                a[e] = pr[8 * h2 + e];
+                b[e] = dsr[8 * h2 + e];
             }
-            pb[s2] = __builtin_convertvector(a, bf16x8);
-            db8[s2] = __builtin_convertvector(b, bf16x8);
+            pb[h2] = __builtin_convertvector(a, bf16x8);
+            sb[h2] = __builtin_convertvector(b, bf16x8);
         }
 
-        // ---- dV^T += dO^T P and dK^T += Q^T dS  (M = dims, N = keys, K = queries)
+        // dV^T += dO^T P and dK^T += Q^T dS (M = dims, N = keys, K = queries 16 s2 + 4hl + {0..3, 8..11})
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) {
 #pragma unroll
             for (int db = 0; db < DB; ++db) {
-                const bf16x8 ao = tr_operand(olds, RP, 16 * s2, 32 * db, lane);
-                dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ao, pb[s2], dva[db], 0, 0, 0);
-                const bf16x8 aq = tr_operand(qlds, RP, 16 * s2, 32 * db, lane);
-                dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(aq, db8[s2], dka[db], 0, 0, 0);
+                const int o = t_lane + L::off(16 * s2, 32 * db);
+                const s16x4 ol = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(osl + o));
+                const s16x4 oh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(osl + o + L::off(8, 0)));
+                const s16x8 ao = {ol[0], ol[1], ol[2], ol[3], oh[0], oh[1], oh[2], oh[3]};
+                dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ao), pb[s2], dva[db],
+                                                                   0, 0, 0);
+                const s16x4 ql4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qsl + o));
+                const s16x4 qh4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qsl + o + L::off(8, 0)));
+                const s16x8 aq = {ql4[0], ql4[1], ql4[2], ql4[3], qh4[0], qh4[1], qh4[2], qh4[3]};
+                dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aq), sb[s2], dka[db],
+                                                                   0, 0, 0);
             }
         }
+        ring_barrier<kPending>();  // item it+1 has landed; this item's slot is free
+    };
 
-        // ---- dS^T (bf16) to LDS: row = key, 4 consecutive queries per write
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int qi = 16 * (i >> 1) + 8 * hl + 4 * (i & 1);
-            f32x4 v4 = {dsr[4 * i], dsr[4 * i + 1], dsr[4 * i + 2], dsr[4 * i + 3]};
-            const bf16x4 b4 = __builtin_convertvector(v4, bf16x4);
-            *reinterpret_cast<bf16x4*>(dst + kk * kDsPitch + qi * 2) = b4;
-        }
-
-        if (it + 1 < n_it) {
-            char* qn = qbuf + (buf ^ 1) * 2 * QT_BYTES;
-            store_q<D>(st, qn, qn + QT_BYTES, auxbuf + (buf ^ 1) * 3 * BQ, tid);
-        }
-        __syncthreads();
-
-        // ---- dQ[:, block] += scale * dS K  (M = queries, N = dims, K = keys)
-        f32x16 dqa = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            const int kb = 16 * (dq_part * KSTEPS + ks);
-            const bf16x8 a = tr_operand(dst, kDsPitch, kb, 0, lane);
-            const bf16x8 b = tr_operand(ktile, RP, kb, 32 * dq_blk, lane);
-            dqa = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dqa, 0, 0, 0);
-        }
-        float* dqh = p.dq + (int64_t)head * D + 32 * dq_blk + ql;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int qi = 8 * (r >> 2) + 4 * hl + (r & 3);
-            if (qi < qrows) unsafeAtomicAdd(dqh + (int64_t)(qrow0 + qi) * p.hq * D, p.scale * dqa[r]);
+    if (n_it > 0) {
+        issue(0, qt0, ot0, ax0);
+        issue(1, qt1, ot1, ax1);
+        issue(2, qt2, ot2, ax2);
+        ring_barrier<kPending>();  // item 0 has landed
+        for (int it = 0; it < n_it; it += 4) {
+            step(it, qt0, ot0, ax0, qt3, ot3, ax3);
+            if (it + 1 < n_it) step(it + 1, qt1, ot1, ax1, qt0, ot0, ax0);
+            if (it + 2 < n_it) step(it + 2, qt2, ot2, ax2, qt1, ot1, ax1);
+            if (it + 3 < n_it) step(it + 3, qt3, ot3, ax3, qt2, ot2, ax2);
         }
     }
 
@@ -449,9 +317,247 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_step_kernel(const BwdParams p
     }
 }
 
+// ============================================================================ dQ
+constexpr int kQWaves = kFwdWaves;  // 8 waves, the forward kernel's shape
+constexpr int kQThreads = 64 * kQWaves;
+constexpr int kBN = 64;
+
+template <int D, int HPW>
+__global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p) {
+    using L = TileLayout<D, kBN>;
+    constexpr int WPH = kQWaves / HPW;
+    constexpr int BMQ = 32 * WPH;
+    constexpr int DS = D / 16;
+    constexpr int DB = D / 32;
+    __shared__ __attribute__((aligned(16))) char kb0[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char kb1[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char kb2[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char kb3[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char vb0[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char vb1[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char vb2[L::BYTES];
+    __shared__ __attribute__((aligned(16))) char vb3[L::BYTES];
+
+    const int tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lane = tid & 63;
+    const int hl = lane >> 5;
+    const int ql = lane & 31;
+
+    const int per_xcd = gridDim.x >> 3;
+    const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    if (w >= p.n_work_q) return;
+    const int hb = w / p.n_qtiles;
+    const int qt = p.n_qtiles - 1 - (w % p.n_qtiles);
+    const int qs = (qt < p.qtiles0) ? 0 : 1;
+    const int qt_in = qs ? qt - p.qtiles0 : qt;
+    const int tile_row0 = p.qs_row0[qs] + qt_in * BMQ;
+    const int tile_pos0 = p.qs_pos0[qs] + qt_in * BMQ;
+    const int tile_rows = min(BMQ, p.qs_len[qs] - qt_in * BMQ);
+    const int q0 = tile_pos0, q1 = tile_pos0 + tile_rows - 1;
+    const int head = hb * HPW + wave / WPH;
+    const int kvh = (hb * HPW) / p.group;
+    const int row_in_tile = (wave % WPH) * 32 + ql;
+    const bool row_valid = row_in_tile < tile_rows;
+    const int my_row = tile_row0 + row_in_tile;
+    const int my_pos = tile_pos0 + row_in_tile;
+
+    const bool any_doc = (p.mask[qs][0] == CP_MASK_DOC) || (p.nkv_seg > 1 && p.mask[qs][1] == CP_MASK_DOC);
+    int lo0 = 0, lo1 = 0, my_lo = 0;
+    if (any_doc) {
+        const int d0 = doc_index(p.cu, p.n_docs, q0);
+        lo0 = p.cu[d0];
+        lo1 = p.cu[doc_index(p.cu, p.n_docs, q1)];
+        int j = d0;
+        if (row_valid) {
+            while (j + 1 < p.n_docs && p.cu[j + 1] <= my_pos) ++j;
+        }
+        my_lo = p.cu[j];
+    }
+    const int mk0 = (p.nkv_seg > 0) ? p.mask[qs][0] : CP_MASK_SKIP;
+    const int mk1 = (p.nkv_seg > 1) ? p.mask[qs][1] : CP_MASK_SKIP;
+    const int len0 = p.ks_len[0], len1 = p.ks_len[1];
+    const int pos0 = p.ks_pos0[0], pos1 = p.ks_pos0[1];
+    const SegRange r0 = key_tile_range<kBN>(mk0, q0, q1, mk0 == CP_MASK_DOC ? lo0 : 0, pos0, len0);
+    const SegRange r1 = (p.nkv_seg > 1) ? key_tile_range<kBN>(mk1, q0, q1, mk1 == CP_MASK_DOC ? lo0 : 0, pos1, len1)
+                                        : SegRange{0, 0};
+    const int tlo0 = r0.t_lo, tlo1 = r1.t_lo;
+    const int n0 = r0.t_hi - r0.t_lo;
+    const int n_it = n0 + (r1.t_hi - r1.t_lo);
+
+    // ---- Q and dO fragments (lane holds query ql, dims 16 ds + 8 hl + 0..7), LSE and delta
+    bf16x8 qf[DS], of[DS];
+    {
+        const int64_t off = ((int64_t)my_row * p.hq + head) * D + 8 * hl;
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds) {
+            u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
+            if (row_valid) {
+                a = *reinterpret_cast<const u32x4*>(p.q + off + 16 * ds);
+                b = *reinterpret_cast<const u32x4*>(p.d_o + off + 16 * ds);
+            }
+            qf[ds] = __builtin_bit_cast(bf16x8, a);
+            of[ds] = __builtin_bit_cast(bf16x8, b);
+        }
+    }
+    float nl = 0.f, dl = 0.f;
+    if (row_valid) {
+        const float l = p.lse[(int64_t)head * p.q_rows + my_row];
+        nl = (l == -INFINITY) ? 0.f : -l * kLog2e;  // a row with no visible key is fully masked
+        dl = p.delta[(int64_t)head * p.q_rows + my_row];
+    }
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    const float c2 = p.scale_log2;
+    const int row_bytes = p.hkv * D * 2;
+    const int64_t head_off = (int64_t)kvh * D;
+    const uint16_t* const kseg0 = p.k + (int64_t)p.ks_row0[0] * p.hkv * D + head_off;
+    const uint16_t* const kseg1 = p.k + (int64_t)p.ks_row0[1] * p.hkv * D + head_off;
+    const uint16_t* const vseg0 = p.v + (int64_t)p.ks_row0[0] * p.hkv * D + head_off;
+    const uint16_t* const vseg1 = p.v + (int64_t)p.ks_row0[1] * p.hkv * D + head_off;
+    const int64_t tile_elems = (int64_t)kBN * p.hkv * D;
+
+    struct TileRef {
+        int t, len, pos, mask, seg;
+    };
+    // by-value capture: a select between captured references becomes a select of
+    // addresses, which the compiler then keeps in (slow) private memory
+    auto tile_of = [=](int it) -> TileRef {
+        const bool second = it >= n0;
+        const int t = second ? tlo1 + (it - n0) : tlo0 + it;
+        return TileRef{t, second ? len1 : len0, second ? pos1 : pos0, second ? mk1 : mk0, second ? 1 : 0};
+    };
+    auto issue = [&](int it, char* kdst, char* vdst) {
+        const TileRef tr = tile_of(it);
+        const bool live = it < n_it;
+        const int rows = live ? min(kBN, tr.len - tr.t * kBN) : 0;
+        const int64_t toff = live ? tr.t * tile_elems : 0;
+        load_tile_lds<D, kBN, kQWaves>(kdst, tile_rsrc((tr.seg ? kseg1 : kseg0) + toff, rows, row_bytes), row_bytes,
+                                       wave, lane);
+        load_tile_lds<D, kBN, kQWaves>(vdst, tile_rsrc((tr.seg ? vseg1 : vseg0) + toff, rows, row_bytes), row_bytes,
+                                       wave, lane);
+    };
+    const int k_lane = L::off(ql, 8 * hl);
+    const int grp = lane >> 4, jl = lane & 15;
+    const int t_lane = L::off(4 * (grp >> 1) + (jl >> 2), 16 * (grp & 1) + 4 * (jl & 3));
+    constexpr int kPending = 2 * 2 * (L::NBLK / kQWaves);
+
+    auto step = [&](int it, const char* ksl, const char* vsl, char* kfill, char* vfill) {
+        issue(it + 3, kfill, vfill);
+        const TileRef tr = tile_of(it);
+        // S^T = K Q^T and dP^T = V dO^T: 64 keys x this wave's 32 queries
+        f32x16 sc[2], dp[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+            sc[kb] = f32x16{};
+            dp[kb] = f32x16{};
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(ksl + k_lane + L::off(32 * kb, 16 * ds));
+                sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sc[kb], 0, 0, 0);
+            }
+#pragma unroll
+            for (int ds = 0; ds < DS; ++ds) {
+                const bf16x8 a = *reinterpret_cast<const bf16x8*>(vsl + k_lane + L::off(32 * kb, 16 * ds));
+                dp[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, of[ds], dp[kb], 0, 0, 0);
+            }
+        }
+        // element mask on partial or ragged tiles, as in the forward kernel
+        const int kcount = min(kBN, tr.len - tr.t * kBN);
+        const int kp0 = tr.pos + tr.t * kBN;
+        const int m = tr.mask;
+        const bool full = key_tile_full<kBN>(m, q0, m == CP_MASK_DOC ? lo1 : 0, tr.pos, tr.len, tr.t);
+        bool vis_all = true;
+        int lo_l = 0;
+        unsigned span = 0;
+        bool none = false;
+        if (!full || kcount < kBN) {
+            vis_all = false;
+            int hi_lim = kcount - 1;
+            int lo_lim = 0;
+            if (m != CP_MASK_FULL) {
+                hi_lim = min(hi_lim, my_pos - kp0);
+                if (m == CP_MASK_DOC) lo_lim = max(0, my_lo - kp0);
+            }
+            lo_l = lo_lim - 4 * hl;
+            span = (unsigned)(hi_lim - lo_lim);
+            none = hi_lim < lo_lim;
+        }
+        // P = exp2(c2 s - log2e LSE), dS = P (dP - delta), rounded to bf16 for dQ
+        bf16x8 sb[4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+            for (int half = 0; half < 2; ++half) {
+                f32x8 v8;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int r = 8 * half + e;
+                    float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c2, nl));
+                    if (!vis_all && (none || (unsigned)(row_of_reg(kb, r, 0) - lo_l) > span)) pv = 0.f;
+                    v8[e] = pv * (dp[kb][r] - dl);
+                }
+                sb[2 * kb + half] = __builtin_convertvector(v8, bf16x8);
+            }
+        }
+        // dQ^T += K^T dS^T: step s4 covers keys 16 s4 + 4hl + {0..3, 8..11}
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) {
+                const char* a0 = ksl + t_lane + L::off(16 * s4, 32 * db);
+                const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+                const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + L::off(8, 0)));
+                const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), sb[s4], acc[db],
+                                                                   0, 0, 0);
+            }
+        }
+        ring_barrier<kPending>();
+    };
+
+    if (n_it > 0) {
+        issue(0, kb0, vb0);
+        issue(1, kb1, vb1);
+        issue(2, kb2, vb2);
+        ring_barrier<kPending>();  // tile 0 has landed
+        for (int it = 0; it < n_it; it += 4) {
+            step(it, kb0, vb0, kb3, vb3);
+            if (it + 1 < n_it) step(it + 1, kb1, vb1, kb0, vb0);
+            if (it + 2 < n_it) step(it + 2, kb2, vb2, kb1, vb1);
+            if (it + 3 < n_it) step(it + 3, kb3, vb3, kb2, vb2);
+        }
+    }
+
+    // ---- dQ[row, head, :] += scale * (dS K)[row, :]; each wave owns its rows
+    if (row_valid && n_it > 0) {
+        float* dqrow = p.dq + ((int64_t)my_row * p.hq + head) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                f32x4* ptr = reinterpret_cast<f32x4*>(dqrow + 32 * db + 8 * i + 4 * hl);
+                f32x4 cur = *ptr;
+                cur.x += p.scale * acc[db][4 * i];
+                cur.y += p.scale * acc[db][4 * i + 1];
+                cur.z += p.scale * acc[db][4 * i + 2];
+                cur.w += p.scale * acc[db][4 * i + 3];
+                *ptr = cur;
+            }
+    }
+}
+
 template <int D>
-hipError_t launch(const BwdParams& prm, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((bwd_step_kernel<D>), dim3(grid), dim3(kThreads), 0, stream, prm);
+hipError_t launch_dkdv(const BwdParams& prm, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(grid), dim3(kKvThreads), 0, stream, prm);
+    return hipGetLastError();
+}
+
+template <int D, int HPW>
+hipError_t launch_dq(const BwdParams& prm, int grid, hipStream_t stream) {
+    hipLaunchKernelGGL((bwd_dq_kernel<D, HPW>), dim3(grid), dim3(kQThreads), 0, stream, prm);
     return hipGetLastError();
 }
 
@@ -465,6 +571,7 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
                                       float* dk_out, float* dv_out, hipStream_t stream) {
     cp_status st = validate_problem(p, true);
     if (st != CP_OK) return st;
+    const TileGeom gq = fwd_geom(p->hq, p->hkv);
     BwdParams prm = {};
     prm.q = static_cast<const uint16_t*>(q);
     prm.k = static_cast<const uint16_t*>(k);
@@ -482,9 +589,10 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     prm.group = p->hq / p->hkv;
     prm.q_rows = int32_t(p->q_rows);
     prm.scale = p->scale;
-    prm.scale_log2 = p->scale * 1.4426950408889634f;
+    prm.scale_log2 = p->scale * kLog2e;
     prm.nq_seg = p->n_q_seg;
-    int64_t nk = 0;
+    prm.nkv_seg = p->n_kv_seg;
+    int64_t nk = 0, nq = 0;
     for (int i = 0; i < 2; ++i) {
         const bool on = i < p->n_q_seg;
         prm.qs_row0[i] = on ? int32_t(p->q_seg[i].row0) : 0;
@@ -495,20 +603,39 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
         prm.ks_pos0[i] = kon ? int32_t(p->kv_seg[i].pos0) : 0;
         prm.ks_len[i] = kon ? int32_t(p->kv_seg[i].len) : 0;
         nk += ceil_div(prm.ks_len[i], BK);
+        nq += ceil_div(prm.qs_len[i], gq.bm);
     }
     for (int i = 0; i < 2; ++i)
         for (int j = 0; j < 2; ++j)
             prm.mask[i][j] = (i < p->n_q_seg && j < p->n_kv_seg) ? p->mask[i][j] : CP_MASK_SKIP;
     prm.ktiles0 = int32_t(ceil_div(prm.ks_len[0], BK));
     prm.n_ktiles = int32_t(nk);
-    const int64_t n_work = nk * p->hkv;
-    if (n_work == 0) return CP_OK;
+    prm.qtiles0 = int32_t(ceil_div(prm.qs_len[0], gq.bm));
+    prm.n_qtiles = int32_t(nq);
+    const int64_t work_kv = nk * p->hkv;
+    const int64_t work_q = nq * (p->hq / gq.hpw);
+    if (work_kv == 0 && work_q == 0) return CP_OK;
     if (!q || !k || !v || !d_o || !lse || !delta || !dq_acc || !dk_out || !dv_out)
         return fail(CP_ERR_INVALID_ARG, "NULL tensor pointer");
-    if (n_work > (int64_t(1) << 30)) return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
-    prm.n_work = int32_t(n_work);
-    const int grid = int(ceil_div(n_work, 8) * 8);
-    hipError_t e = (p->head_dim == 128) ? launch<128>(prm, grid, stream) : launch<64>(prm, grid, stream);
-    if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd launch: ") + hipGetErrorString(e));
+    if (work_kv > (int64_t(1) << 30) || work_q > (int64_t(1) << 30))
+        return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
+    prm.n_work_kv = int32_t(work_kv);
+    prm.n_work_q = int32_t(work_q);
+    hipError_t e = hipSuccess;
+    if (work_kv > 0) {
+        const int grid = int(ceil_div(work_kv, 8) * 8);
+        e = (p->head_dim == 128) ? launch_dkdv<128>(prm, grid, stream) : launch_dkdv<64>(prm, grid, stream);
+        if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd dK/dV launch: ") + hipGetErrorString(e));
+    }
+    if (work_q > 0) {
+        const int grid = int(ceil_div(work_q, 8) * 8);
+        if (p->head_dim == 128)
+            e = (gq.hpw == 4) ? launch_dq<128, 4>(prm, grid, stream)
+                              : (gq.hpw == 2 ? launch_dq<128, 2>(prm, grid, stream) : launch_dq<128, 1>(prm, grid, stream));
+        else
+            e = (gq.hpw == 4) ? launch_dq<64, 4>(prm, grid, stream)
+                              : (gq.hpw == 2 ? launch_dq<64, 2>(prm, grid, stream) : launch_dq<64, 1>(prm, grid, stream));
+        if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd dQ launch: ") + hipGetErrorString(e));
+    }
     return CP_OK;
 }

@@ -6,47 +6,40 @@
 // Attention Algorithms").
 //
 // Design (gfx950, wave64, 32x32x16 bf16 MFMA with fp32 accumulation):
-//  * A workgroup is 4 waves.  Each wave owns 32 query rows of one query head;
-//    HPW heads of one GQA group share the workgroup, so every K/V tile staged
-//    in LDS serves HPW heads (BMQ = 128 / HPW rows per workgroup tile).
+//  * One 8-wave workgroup per CU (2 waves per SIMD).  Each wave owns 32 query
+//    rows of one query head; HPW heads of one GQA group share the workgroup,
+//    so every K/V tile staged in LDS serves 256 query-row-heads.
 //  * Scores are computed transposed, S^T = K Q^T (keys on the MFMA M axis,
-//    queries on N): each lane then holds one query and 32 of its keys, so the
-//    row max needs a single exchange between the two half-waves and the row
-//    sum needs none until the epilogue.
-//  * The P registers, rounded to bf16, are directly the B operand of the P V
-//    product (O^T = V^T P^T).  V stays row-major in LDS; its transposed MFMA
-//    operand comes from the gfx950 transposing LDS read (ds_read_tr16_b64:
-//    16 lanes read a 4-row x 16-column block and each lane receives 4
-//    consecutive rows of one column), two reads per MFMA.
-//  * K/V tiles are fetched with buffer loads (rows past the end of a ragged
-//    tile read as zero through the descriptor's range check), double-buffered
-//    in LDS with rows padded so that every operand read is conflict-free and a
-//    base register plus an immediate offset; the loads of tile i+1 are issued
-//    before the MFMAs of tile i.
-//  * The running maximum is only raised when a row's maximum grows by more
+//    queries on N): each lane holds one query and 32 of its keys, so the row
+//    max needs one exchange between the half-waves and the row sum none until
+//    the epilogue.  The P registers, rounded to bf16, are directly the B
+//    operand of O^T += V^T P^T; V stays row-major in LDS and its transposed
+//    operand comes from the transposing LDS read (ds_read_tr16_b64).
+//  * K/V tiles move HBM -> LDS with direct buffer loads (rows past a ragged
+//    tile read as zero) into a ring of four K and four V buffers, three tiles
+//    ahead of use; each step waits only for the tiles the next step reads.
+//  * Rotated pipeline: the P V product of tile i-1 overlaps the mask and row
+//    max of tile i; the scores of tile i+1 overlap the exponentials of tile i.
+//  * The reference maximum is raised only when a row's maximum grows by more
 //    than 2^8 in the exp2 domain, so the accumulator is rescaled rarely; P is
 //    then bounded by 256, which fp32 accumulation and bf16 rounding absorb.
 //  * Tiles with no visible pair are never visited (block-sparse skip); the
-//    element mask is applied only to partially visible or ragged tiles.
-//  * Workgroup ids are mapped so each XCD (ids equal mod 8) works on one
-//    range of head blocks (sharing K/V in its L2), latest positions first.
+//    element mask runs only on partially visible or ragged tiles.
+//  * Workgroup ids map each XCD (ids equal mod 8) to one range of head blocks
+//    (K/V shared in its L2), latest query positions first.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
 #include <cstdint>
 
 #include "internal.h"
+#include "tiles.h"
 
 namespace cpattn {
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+using namespace dev;
 
 constexpr int kBN = 64;                    // keys per tile
 constexpr int kWaves = kFwdWaves;          // 8 waves: 2 per SIMD, one workgroup per CU
@@ -74,103 +67,9 @@ struct FwdParams {
     int32_t n_work;
 };
 
-// Key (within a 64-key tile) held by score register r = 4i + j of key block kb
-// in half hl of the wave: the 32x32 MFMA output row 8i + 4hl + j.  Registers
-// 8(s%2)..8(s%2)+7 of block s/2 hold keys 16s + 4hl + {0..3, 8..11}: the B
-// operand of P V step s, matched by two transposing reads of V rows.
-__device__ __forceinline__ int key_of_reg(int kb, int r, int hl) {
-    return 32 * kb + 8 * (r >> 2) + 4 * hl + (r & 3);
-}
-
-__device__ __forceinline__ int doc_index(const int32_t* cu, int n_docs, int pos) {
-    int lo = 0, hi = n_docs - 1;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (cu[mid] <= pos)
-            lo = mid;
-        else
-            hi = mid - 1;
-    }
-    return lo;
-}
-
-struct SegRange {
-    int t_lo, t_hi;
-};
-
-// Mirror of the host tile_range rule (global positions, q1 = last row).
-__device__ __forceinline__ SegRange seg_range(int mask, int q0, int q1, int lo0, int kpos0, int klen) {
-    const int nkt = (klen + kBN - 1) / kBN;
-    if (mask == CP_MASK_SKIP || klen == 0) return {0, 0};
-    if (mask == CP_MASK_FULL) return {0, nkt};
-    const int t_hi = (q1 < kpos0) ? 0 : min(nkt, (q1 - kpos0) / kBN + 1);
-    int t_lo = 0;
-    if (lo0 > kpos0) {
-        if (lo0 > kpos0 + klen - 1) return {0, 0};
-        t_lo = (lo0 - kpos0) / kBN;
-    }
-    if (t_lo >= t_hi) return {0, 0};
-    return {t_lo, t_hi};
-}
-
-__device__ __forceinline__ bool tile_full(int mask, int q0, int lo1, int kpos0, int klen, int t) {
-    if (mask == CP_MASK_FULL) return true;
-    const int k0 = kpos0 + t * kBN;
-    const int k1 = min(kpos0 + klen, k0 + kBN) - 1;
-    return k1 <= q0 && k0 >= lo1;
-}
-
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-typedef short s16x8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// LDS tile layout.  One buffer load per wave moves 1 KiB (64 lanes x 16 B)
-// straight into LDS, lane i landing at base + 16 i; that KiB holds RB = 1024 /
-// (2D) consecutive rows, stored chunk-major: (row j, 16-byte chunk c) at
-// 16 (RB c + j).  Blocks are BLK bytes apart; the padding makes the 16-byte
-// operand reads of 16 consecutive rows and the transposing reads of a 4 x 16
-// block hit distinct banks.
-template <int D>
-struct TileLayout {
-    static constexpr int RB = 1024 / (2 * D);
-    static constexpr int BLK = 1024 + (D == 128 ? 64 : 128);
-    static constexpr int NBLK = kBN / RB;
-    static constexpr int BYTES = NBLK * BLK;
-    // byte offset of element (row, col) of a tile
-    static __device__ __forceinline__ int off(int row, int col) {
-        return (row / RB) * BLK + 16 * (RB * (col / 8) + row % RB) + 2 * (col % 8);
-    }
-};
-
-// Buffer descriptor covering rows [0, rows) of one head of a [rows, H, D] bf16
-// tensor starting at `base`: reads of later rows return zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int rows, int row_bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, rows * row_bytes, 0x00020000);
-}
-
-// Issue the direct-to-LDS loads of one 64-row tile (this wave's blocks): every
-// wave issues exactly kLoadsPerTile loads per tile, which the wait counts rely on.
-template <int D>
-constexpr int loads_per_tile() { return TileLayout<D>::NBLK / kWaves; }
-
-template <int D>
-__device__ __forceinline__ void load_tile_lds(char* dst, __amdgpu_buffer_rsrc_t rs, int row_bytes, int wave, int lane) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    using L = TileLayout<D>;
-    const int j = lane % L::RB, c = lane / L::RB;
-#pragma unroll
-    for (int b = 0; b < loads_per_tile<D>(); ++b) {
-        const int blk = wave + kWaves * b;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + blk * L::BLK), 16,
-                                                 (blk * L::RB + j) * row_bytes + c * 16, 0, 0, 0);
-    }
-#endif
-}
-
 template <int D, int HPW>
 __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p) {
-    using L = TileLayout<D>;
+    using L = TileLayout<D, kBN>;
     constexpr int WPH = kWaves / HPW; // waves per head
     constexpr int BMQ = 32 * WPH;     // query rows per workgroup tile
     constexpr int DS = D / 16;        // MFMA k-steps over the head dim
@@ -233,7 +132,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     for (int s = 0; s < 2; ++s) {
         mk[s] = (s < p.nkv_seg) ? p.mask[qs][s] : CP_MASK_SKIP;
         const bool doc = (mk[s] == CP_MASK_DOC);
-        rng[s] = (s < p.nkv_seg) ? seg_range(mk[s], q0, q1, doc ? lo0 : 0, p.ks_pos0[s], p.ks_len[s])
+        rng[s] = (s < p.nkv_seg) ? key_tile_range<kBN>(mk[s], q0, q1, doc ? lo0 : 0, p.ks_pos0[s], p.ks_len[s])
                                  : SegRange{0, 0};
     }
 
@@ -243,7 +142,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
             const int t = s ? col - p.ktiles0 : col;
             uint8_t c = CP_TILE_SKIP;
             if (t >= rng[s].t_lo && t < rng[s].t_hi)
-                c = tile_full(mk[s], q0, mk[s] == CP_MASK_DOC ? lo1 : 0, p.ks_pos0[s], p.ks_len[s], t)
+                c = key_tile_full<kBN>(mk[s], q0, mk[s] == CP_MASK_DOC ? lo1 : 0, p.ks_pos0[s], p.ks_len[s], t)
                         ? CP_TILE_FULL
                         : CP_TILE_PARTIAL;
             p.tile_map[(int64_t)qt * p.n_ktiles + col] = c;
@@ -322,14 +221,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         }
     };
 
-    // Wait until at most `pending` of this wave's loads are in flight (and
-    // every LDS read has completed), then synchronise the workgroup.
-    constexpr int kPending = 2 * 2 * loads_per_tile<D>();  // the loads of the last two steps
-    auto ring_barrier = [&]() {
-        // s_waitcnt: vmcnt = kPending (bits 3:0 and 15:14), expcnt 7 (no wait), lgkmcnt 0
-        __builtin_amdgcn_s_waitcnt((kPending & 15) | ((kPending >> 4) << 14) | (7 << 4));
-        __builtin_amdgcn_s_barrier();
-    };
+    // At each step's barrier the loads of the last two steps may still be in
+    // flight; everything older (the tiles the next step reads) has landed.
+    constexpr int kPending = 2 * 2 * (L::NBLK / kWaves);
 
     bf16x8 pb[4];  // P of the previous tile (bf16), consumed by the next step's P V
     // Rotated pipeline step `it` (0 <= it <= n_it):
@@ -341,8 +235,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     // touches statically known buffers.
     auto step = [&](int it, f32x16* cur, f32x16* nxt, char* k_fill, const char* k_read, char* v_fill,
                     const char* v_read) {
-        load_tile_lds<D>(k_fill, rsrc_of(false, it + 4), row_bytes, wave, lane);
-        load_tile_lds<D>(v_fill, rsrc_of(true, it + 2), row_bytes, wave, lane);
+        load_tile_lds<D, kBN, kWaves>(k_fill, rsrc_of(false, it + 4), row_bytes, wave, lane);
+        load_tile_lds<D, kBN, kWaves>(v_fill, rsrc_of(true, it + 2), row_bytes, wave, lane);
 
         if (it >= 1) {
             // O^T += V^T P^T: step s4 covers keys 16 s4 + 4hl + {0..3, 8..11}
@@ -368,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
             const int kcount = min(kBN, tr.len - tr.t * kBN);
             const int kp0 = tr.pos + tr.t * kBN;
             const int m = tr.mask;
-            const bool full = tile_full(m, q0, m == CP_MASK_DOC ? lo1 : 0, tr.pos, tr.len, tr.t);
+            const bool full = key_tile_full<kBN>(m, q0, m == CP_MASK_DOC ? lo1 : 0, tr.pos, tr.len, tr.t);
             if (!full || kcount < kBN) {
                 int hi_lim = kcount - 1;
                 int lo_lim = 0;
@@ -383,7 +277,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
                 for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key0 = key_of_reg(kb, r, 0);
+                        const int key0 = row_of_reg(kb, r, 0);
                         if (none || (unsigned)(key0 - lo_l) > span) cur[kb][r] = -INFINITY;
                     }
             }
@@ -426,21 +320,21 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
             }
             l_run += (part[0] + part[1]) + (part[2] + part[3]);
         }
-        ring_barrier();  // the tiles the next step reads have landed; this step's slots are free
+        ring_barrier<kPending>();  // the tiles the next step reads have landed; this step's slots are free
     };
 
     f32x16 sa[2], sb[2];
     if (n_it > 0) {
-        load_tile_lds<D>(kb0, rsrc_of(false, 0), row_bytes, wave, lane);
-        load_tile_lds<D>(kb1, rsrc_of(false, 1), row_bytes, wave, lane);
+        load_tile_lds<D, kBN, kWaves>(kb0, rsrc_of(false, 0), row_bytes, wave, lane);
+        load_tile_lds<D, kBN, kWaves>(kb1, rsrc_of(false, 1), row_bytes, wave, lane);
         __syncthreads();
         scores(kb0, sa);
         // issue order matters for the wait counts: V0, K2, V1, K3, then two per step
-        load_tile_lds<D>(vb0, rsrc_of(true, 0), row_bytes, wave, lane);
-        load_tile_lds<D>(kb2, rsrc_of(false, 2), row_bytes, wave, lane);
-        load_tile_lds<D>(vb1, rsrc_of(true, 1), row_bytes, wave, lane);
-        load_tile_lds<D>(kb3, rsrc_of(false, 3), row_bytes, wave, lane);
-        ring_barrier();  // K(1) and V(0) have landed; every wave has read K(0)
+        load_tile_lds<D, kBN, kWaves>(vb0, rsrc_of(true, 0), row_bytes, wave, lane);
+        load_tile_lds<D, kBN, kWaves>(kb2, rsrc_of(false, 2), row_bytes, wave, lane);
+        load_tile_lds<D, kBN, kWaves>(vb1, rsrc_of(true, 1), row_bytes, wave, lane);
+        load_tile_lds<D, kBN, kWaves>(kb3, rsrc_of(false, 3), row_bytes, wave, lane);
+        ring_barrier<kPending>();  // K(1) and V(0) have landed; every wave has read K(0)
         for (int it = 0; it <= n_it; it += 4) {
             step(it, sa, sb, kb0, kb1, vb2, vb3);
             if (it + 1 <= n_it) step(it + 1, sb, sa, kb1, kb2, vb3, vb0);
