@@ -9,7 +9,11 @@ tokens as two zigzag 8K chunks, 8 ring steps).  Inputs are seeded synthetic
 N(0,1) values rounded to bf16, resident in HBM before timing starts.
 
 Prints one JSON line.  FLOPs are causal-counted: 4*D per visible (query, key)
-pair and query head for the forward.
+pair and query head for the forward.  The roofline object's ``traffic`` is the
+HBM traffic per launch of the forward kernel from the committed FETCH_SIZE /
+WRITE_SIZE summary under profiles/, when that summary was taken on the current
+kernel sources (else null); ``--calibrate-copy-mib`` makes the known-size
+copies that summary is scaled by.
 """
 from __future__ import annotations
 
@@ -109,6 +113,29 @@ def cpu_baseline(w, rank, heads):
             "seconds": dt, "flops": flops}
 
 
+def fwd_algorithmic_bytes(w):
+    """Bytes one forward step launch must move at least: Q, K and V read once (bf16),
+    the step's O (fp32) and LSE (fp32) written once."""
+    q = w.local * w.hq * w.dim * 2
+    kv = 2 * w.local * w.hkv * w.dim * 2
+    o = w.local * w.hq * w.dim * 4
+    lse = w.hq * w.local * 4
+    return q + kv + o + lse
+
+
+def calibration_copies(torch, mib, count=3):
+    """Plain device-to-device copies of a known size, made before any other GPU
+    work so that they are the first copy dispatches a counter run records."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(count):
+        dst.copy_(src)
+    torch.zeros(1, device="cuda")  # a non-copy dispatch marks the end of the calibration
+    torch.cuda.synchronize()
+    log(f"calibration: {count} copies of {mib} MiB")
+    del src, dst
+
+
 def measure(torch, w, rank, steps, warmup, backward):
     """Time `steps` whole-rank passes (forward ring, plus the backward ring if asked)."""
     from context_long_attention_amd.ring import RankRing
@@ -165,6 +192,13 @@ def measure(torch, w, rank, steps, warmup, backward):
     return out
 
 
+def _hpw(w):
+    """Query heads per forward workgroup (the kernel's second template argument)."""
+    from context_long_attention_amd import cpattn
+    bm, _ = cpattn.cp_tile_shape(w.hq, w.hkv, w.dim)
+    return 256 // bm
+
+
 def tflops(flops, ms):
     return flops / (ms * 1e-3) / 1e12
 
@@ -180,6 +214,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="first make 3 device-to-device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU (one rank's share of the ring); --gpus {args.gpus} "
@@ -187,15 +223,20 @@ def main():
         sys.exit(2)
 
     import torch
-    from context_long_attention_amd import cpattn, inputs
+    from context_long_attention_amd import cpattn, inputs, profsum
 
     cpattn.lib()
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib > 0:
+        calibration_copies(torch, args.calibrate_copy_mib)
     w = inputs.WORKLOADS[args.workload]
     log(f"workload {w.name}: S={w.seq_len} CP={w.cp} Hq={w.hq} Hkv={w.hkv} D={w.dim} rank={args.rank}")
     fwd = measure(torch, w, args.rank, args.steps, args.warmup, backward=False)
     value = tflops(fwd["flops_fwd"], fwd["ms"])
     achieved = tflops(fwd["flops_fwd"], fwd["fwd_kernel_ms"])
+    kernel = f"fwd_step_kernel<{w.dim}, {_hpw(w)}>"
+    prof = os.path.join(ROOT, "profiles", f"fwd_step_kernel_{w.name}_traffic.md")
+    measured = profsum.read_traffic(prof, kernel, w.name)
     record = {
         "metric": "causal attention TFLOP/s per ring-step share (fwd, fwd+bwd); % bf16 MFMA peak",
         "value": round(value, 2),
@@ -216,9 +257,12 @@ def main():
         "kernel_only": {"tflops": round(achieved, 2), "pct_bf16_peak": round(100 * achieved / BF16_PEAK_TFLOPS, 2),
                         "ms_per_step": round(fwd["fwd_kernel_ms"], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "fwd_step_kernel<128,4>",
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured["traffic_bytes_per_launch"] if measured else None,
+                     "kernel": kernel,
                      "flops_per_launch": fwd["flops_fwd"] / fwd["launches"],
+                     "algorithmic_bytes_per_launch": fwd_algorithmic_bytes(w),
+                     "traffic_source": os.path.relpath(prof, ROOT) if measured else None,
                      "avg_launch_ms": round(fwd["fwd_kernel_ms"] / fwd["launches"], 4)},
     }
     if not args.no_bwd:

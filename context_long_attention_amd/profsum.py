@@ -1,0 +1,234 @@
+"""Short text summaries of rocprofv3 CSV output, and the traffic lookup bench.py uses.
+
+Two summaries are produced (both are markdown with the exact commands that made
+them):
+
+* ``stats``: the per-kernel table of a ``rocprofv3 --kernel-trace --stats
+  --output-format csv`` run (calls, total, average, min, max duration).
+* ``traffic``: HBM traffic of one kernel from two ``--pmc`` runs (``FETCH_SIZE``
+  and ``WRITE_SIZE``, KiB per dispatch).  The raw counters are scaled by what
+  the same counters read for a plain device-to-device copy of known size made
+  at the start of the same program (``bench.py --calibrate-copy-mib``), so the
+  result is in bytes of memory traffic per launch.  The summary records a
+  SHA-256 of the kernel's source files; ``read_traffic`` returns the figure
+  only while those sources are unchanged.
+
+Usage::
+
+    python -m context_long_attention_amd.profsum stats --csv K_kernel_stats.csv \
+        --command "<rocprofv3 command>" --out profiles/NAME.md
+    python -m context_long_attention_amd.profsum traffic --fetch F.csv --write W.csv \
+        --kernel "fwd_step_kernel<128, 4>" --workload llama3_8b_fwd --copy-mib 1024 \
+        --command "<fetch command>" --command "<write command>" --out profiles/NAME.md
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import json
+import os
+import re
+from collections import defaultdict
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+
+# source files that define each kernel whose traffic may be reported
+KERNEL_SOURCES = {
+    "fwd_step_kernel": ["context_long_attention_amd/csrc/attn_fwd.hip", "context_long_attention_amd/csrc/tiles.h",
+                        "context_long_attention_amd/csrc/internal.h"],
+    "bwd_dkdv_kernel": ["context_long_attention_amd/csrc/attn_bwd.hip", "context_long_attention_amd/csrc/tiles.h",
+                        "context_long_attention_amd/csrc/internal.h"],
+    "bwd_dq_kernel": ["context_long_attention_amd/csrc/attn_bwd.hip", "context_long_attention_amd/csrc/tiles.h",
+                      "context_long_attention_amd/csrc/internal.h"],
+    "merge_kernel": ["context_long_attention_amd/csrc/merge.hip"],
+}
+COPY_KERNEL = "copyBuffer"
+
+
+def _family(kernel: str) -> str:
+    for fam in KERNEL_SOURCES:
+        if fam in kernel:
+            return fam
+    raise KeyError(f"no source list for kernel {kernel!r}")
+
+
+def source_digest(kernel: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[_family(kernel)]:
+        h.update(rel.encode())
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def short_name(name: str) -> str:
+    """``void ns::(anonymous namespace)::fwd_step_kernel<128, 4>(Params)`` -> ``fwd_step_kernel<128, 4>``."""
+    n = re.sub(r"^void\s+", "", name).replace("(anonymous namespace)::", "")
+    depth = 0
+    for i, ch in enumerate(n):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            n = n[:i]
+            break
+    head, sep, tail = n.partition("<")
+    return head.split("::")[-1] + sep + tail
+
+
+def kernel_stats(path: str):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            rows.append({"name": short_name(r["Name"]), "calls": int(r["Calls"]),
+                         "total_ms": float(r["TotalDurationNs"]) / 1e6, "avg_ms": float(r["AverageNs"]) / 1e6,
+                         "min_ms": float(r["MinNs"]) / 1e6, "max_ms": float(r["MaxNs"]) / 1e6,
+                         "pct": float(r["Percentage"])})
+    rows.sort(key=lambda r: -r["total_ms"])
+    return rows
+
+
+def stats_markdown(path: str, commands, top: int = 12, title: str | None = None) -> str:
+    rows = kernel_stats(path)
+    out = [f"# {title or 'Kernel trace summary'}", "", "Made by:", ""]
+    out += ["```", *commands, "```", ""]
+    out += ["| kernel | calls | total ms | avg ms | min ms | max ms | % |", "|---|---:|---:|---:|---:|---:|---:|"]
+    for r in rows[:top]:
+        out.append(f"| `{r['name']}` | {r['calls']} | {r['total_ms']:.3f} | {r['avg_ms']:.4f} | {r['min_ms']:.4f} | "
+                   f"{r['max_ms']:.4f} | {r['pct']:.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def counters_by_dispatch(path: str, counter: str):
+    """kernel short name -> list of (dispatch id, value summed over the counter's instances)."""
+    acc = defaultdict(float)
+    names = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] != counter:
+                continue
+            d = int(r["Dispatch_Id"])
+            acc[d] += float(r["Counter_Value"])
+            names[d] = short_name(r["Kernel_Name"])
+    out = defaultdict(list)
+    for d in sorted(acc):
+        out[names[d]].append((d, acc[d]))
+    return out
+
+
+def _copy_calibration(by_kernel, copy_count: int):
+    """Counter total of the calibration copies: the leading run of copy dispatches
+    before the first dispatch of any other kernel (the program makes them first and
+    then launches a one-element fill).  A copy split over several dispatches is
+    summed whole."""
+    order = sorted((d, name, v) for name, vals in by_kernel.items() for d, v in vals)
+    lead = []
+    for d, name, v in order:
+        if COPY_KERNEL not in name:
+            break
+        lead.append(v)
+    if len(lead) < copy_count or len(lead) % copy_count:
+        raise SystemExit(f"found {len(lead)} leading {COPY_KERNEL} dispatches, expected a multiple of {copy_count}")
+    per = len(lead) // copy_count
+    copies = [sum(lead[i * per:(i + 1) * per]) for i in range(copy_count)]
+    spread = (max(copies) - min(copies)) / max(copies)
+    if spread > 0.02:
+        raise SystemExit(f"calibration copies disagree by {100 * spread:.1f}%: {copies}")
+    return sum(copies) / copy_count
+
+
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int, copy_count: int = 3):
+    fetch = counters_by_dispatch(fetch_csv, "FETCH_SIZE")
+    write = counters_by_dispatch(write_csv, "WRITE_SIZE")
+    copy_fetch = _copy_calibration(fetch, copy_count)
+    copy_write = _copy_calibration(write, copy_count)
+    kf = [v for name, vals in fetch.items() if name == kernel for _, v in vals]
+    kw = [v for name, vals in write.items() if name == kernel for _, v in vals]
+    if not kf or not kw:
+        raise SystemExit(f"kernel {kernel!r} not in the counter files (have {sorted(fetch)})")
+    copy_kib = copy_bytes / 1024.0
+    fs, ws = copy_kib / copy_fetch, copy_kib / copy_write
+    f_kib, w_kib = sum(kf) / len(kf), sum(kw) / len(kw)
+    return {"kernel": kernel, "dispatches": len(kf),
+            "fetch_kib_per_dispatch": round(f_kib, 1), "write_kib_per_dispatch": round(w_kib, 1),
+            "copy_bytes": copy_bytes, "copy_fetch_kib": round(copy_fetch, 1), "copy_write_kib": round(copy_write, 1),
+            "fetch_scale": round(fs, 4), "write_scale": round(ws, 4),
+            "fetch_bytes_per_launch": round(f_kib * fs * 1024),
+            "write_bytes_per_launch": round(w_kib * ws * 1024),
+            "traffic_bytes_per_launch": round((f_kib * fs + w_kib * ws) * 1024),
+            "source_sha256": source_digest(kernel)}
+
+
+def traffic_markdown(t: dict, workload: str, commands, algorithmic_bytes: int | None = None) -> str:
+    t = dict(t, workload=workload)
+    if algorithmic_bytes:
+        t["algorithmic_bytes_per_launch"] = algorithmic_bytes
+        t["traffic_over_algorithmic"] = round(t["traffic_bytes_per_launch"] / algorithmic_bytes, 3)
+    out = [f"# HBM traffic of `{t['kernel']}` on {workload}", "", "Made by (one counter per run):", ""]
+    out += ["```", *commands, "```", ""]
+    out += [f"- raw counters per dispatch (average of {t['dispatches']}): FETCH_SIZE {t['fetch_kib_per_dispatch']} KiB,"
+            f" WRITE_SIZE {t['write_kib_per_dispatch']} KiB",
+            f"- calibration: a {t['copy_bytes'] / 2**20:.0f} MiB device-to-device copy reads as FETCH_SIZE "
+            f"{t['copy_fetch_kib']} KiB and WRITE_SIZE {t['copy_write_kib']} KiB, so the scale factors are "
+            f"{t['fetch_scale']} and {t['write_scale']}",
+            f"- traffic per launch: {t['fetch_bytes_per_launch'] / 2**20:.1f} MiB read + "
+            f"{t['write_bytes_per_launch'] / 2**20:.1f} MiB written = {t['traffic_bytes_per_launch'] / 2**20:.1f} MiB"]
+    if algorithmic_bytes:
+        out.append(f"- algorithmic bytes per launch: {algorithmic_bytes / 2**20:.1f} MiB "
+                   f"(ratio {t['traffic_over_algorithmic']})")
+    out += ["", "```json", json.dumps(t, indent=1), "```", ""]
+    return "\n".join(out)
+
+
+def read_traffic(path: str, kernel: str, workload: str):
+    """Measured traffic (bytes per launch) from a traffic summary, or None when the
+    summary is missing, is for another kernel or workload, or the kernel's sources
+    changed since the counters were taken."""
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), flags=re.S)
+    if not m:
+        return None
+    t = json.loads(m.group(1))
+    if t.get("kernel") != kernel or t.get("workload") != workload:
+        return None
+    if t.get("source_sha256") != source_digest(kernel):
+        return None
+    return t
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--command", action="append", default=[])
+    s.add_argument("--title")
+    s.add_argument("--top", type=int, default=12)
+    s.add_argument("--out", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", required=True)
+    t.add_argument("--workload", required=True)
+    t.add_argument("--copy-mib", type=int, required=True)
+    t.add_argument("--copy-count", type=int, default=3)
+    t.add_argument("--algorithmic-bytes", type=int)
+    t.add_argument("--command", action="append", default=[])
+    t.add_argument("--out", required=True)
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        text = stats_markdown(a.csv, a.command, a.top, a.title)
+    else:
+        tr = traffic(a.fetch, a.write, a.kernel, a.copy_mib << 20, a.copy_count)
+        text = traffic_markdown(tr, a.workload, a.command, a.algorithmic_bytes)
+    with open(a.out, "w") as f:
+        f.write(text)
+    print(text)
+
+
+if __name__ == "__main__":
+    main()
