@@ -101,9 +101,24 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     const int qt = p.n_qtiles - 1 - (w % p.n_qtiles);
     const int qs = (qt < p.qtiles0) ? 0 : 1;
     const int qt_in = qs ? qt - p.qtiles0 : qt;
-    const int tile_row0 = p.qs_row0[qs] + qt_in * BMQ;
-    const int tile_pos0 = p.qs_pos0[qs] + qt_in * BMQ;
-    const int tile_rows = min(BMQ, p.qs_len[qs] - qt_in * BMQ);
+    // Segment parameters as opaque scalars; nothing below indexes the parameter
+    // arrays with a runtime value (see sreg).
+    const int qrow0_a = sreg(p.qs_row0[0]), qrow0_b = sreg(p.qs_row0[1]);
+    const int qpos0_a = sreg(p.qs_pos0[0]), qpos0_b = sreg(p.qs_pos0[1]);
+    const int qlen_a = sreg(p.qs_len[0]), qlen_b = sreg(p.qs_len[1]);
+    const int m00 = sreg(p.mask[0][0]), m01 = sreg(p.mask[0][1]);
+    const int m10 = sreg(p.mask[1][0]), m11 = sreg(p.mask[1][1]);
+    const int len0 = sreg(p.ks_len[0]), len1 = sreg(p.ks_len[1]);
+    const int pos0 = sreg(p.ks_pos0[0]), pos1 = sreg(p.ks_pos0[1]);
+    const int krow0 = sreg(p.ks_row0[0]), krow1 = sreg(p.ks_row0[1]);
+    const int qrow0 = qs ? qrow0_b : qrow0_a;
+    const int qpos0 = qs ? qpos0_b : qpos0_a;
+    const int qlen = qs ? qlen_b : qlen_a;
+    const int mk0 = qs ? m10 : m00;  // the host marks absent KV segments SKIP
+    const int mk1 = qs ? m11 : m01;
+    const int tile_row0 = qrow0 + qt_in * BMQ;
+    const int tile_pos0 = qpos0 + qt_in * BMQ;
+    const int tile_rows = min(BMQ, qlen - qt_in * BMQ);
     const int q0 = tile_pos0, q1 = tile_pos0 + tile_rows - 1;
 
     const int head = hb * HPW + wave / WPH;
@@ -114,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     const int my_pos = tile_pos0 + row_in_tile;
 
     // ---- tile ranges of the (up to) two KV segments
-    const bool any_doc = (p.mask[qs][0] == CP_MASK_DOC) || (p.nkv_seg > 1 && p.mask[qs][1] == CP_MASK_DOC);
+    const bool any_doc = (mk0 == CP_MASK_DOC) || (mk1 == CP_MASK_DOC);
     int lo0 = 0, lo1 = 0, my_lo = 0;
     if (any_doc) {
         const int d0 = doc_index(p.cu, p.n_docs, q0);
@@ -126,31 +141,31 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         }
         my_lo = p.cu[j];
     }
-    SegRange rng[2];
-    int mk[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        mk[s] = (s < p.nkv_seg) ? p.mask[qs][s] : CP_MASK_SKIP;
-        const bool doc = (mk[s] == CP_MASK_DOC);
-        rng[s] = (s < p.nkv_seg) ? key_tile_range<kBN>(mk[s], q0, q1, doc ? lo0 : 0, p.ks_pos0[s], p.ks_len[s])
-                                 : SegRange{0, 0};
-    }
+    const SegRange r0 = key_tile_range<kBN>(mk0, q0, q1, mk0 == CP_MASK_DOC ? lo0 : 0, pos0, len0);
+    const SegRange r1 = key_tile_range<kBN>(mk1, q0, q1, mk1 == CP_MASK_DOC ? lo0 : 0, pos1, len1);
+    const int tlo0 = r0.t_lo, thi0 = r0.t_hi, tlo1 = r1.t_lo, thi1 = r1.t_hi;
+    // tiles of each segment that need no element mask
+    const SegRange f0r = full_tile_range<kBN>(mk0, q0, mk0 == CP_MASK_DOC ? lo1 : 0, pos0, len0);
+    const SegRange f1r = full_tile_range<kBN>(mk1, q0, mk1 == CP_MASK_DOC ? lo1 : 0, pos1, len1);
+    const int flo0 = f0r.t_lo, fn0 = f0r.t_hi - f0r.t_lo;
+    const int flo1 = f1r.t_lo, fn1 = f1r.t_hi - f1r.t_lo;
 
     if (p.tile_map) {
         for (int col = tid; col < p.n_ktiles; col += kThreads) {
-            const int s = (col < p.ktiles0) ? 0 : 1;
-            const int t = s ? col - p.ktiles0 : col;
+            const bool sec = col >= p.ktiles0;
+            const int t = sec ? col - p.ktiles0 : col;
+            const int m = sec ? mk1 : mk0;
             uint8_t c = CP_TILE_SKIP;
-            if (t >= rng[s].t_lo && t < rng[s].t_hi)
-                c = key_tile_full<kBN>(mk[s], q0, mk[s] == CP_MASK_DOC ? lo1 : 0, p.ks_pos0[s], p.ks_len[s], t)
+            if (t >= (sec ? tlo1 : tlo0) && t < (sec ? thi1 : thi0))
+                c = key_tile_full<kBN>(m, q0, m == CP_MASK_DOC ? lo1 : 0, sec ? pos1 : pos0, sec ? len1 : len0, t)
                         ? CP_TILE_FULL
                         : CP_TILE_PARTIAL;
             p.tile_map[(int64_t)qt * p.n_ktiles + col] = c;
         }
     }
 
-    const int n0 = rng[0].t_hi - rng[0].t_lo;
-    const int n_it = n0 + (rng[1].t_hi - rng[1].t_lo);
+    const int n0 = thi0 - tlo0;
+    const int n_it = n0 + (thi1 - tlo1);
 
     // ---- Q fragment in registers: lane holds query ql, dims 16*ds + 8*hl + 0..7
     bf16x8 qf[DS];
@@ -172,35 +187,40 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     const float c2 = p.scale_log2;
     const int row_bytes = p.hkv * D * 2;
 
-    // Per-segment values held in scalars for the whole tile loop (a runtime
-    // index into the parameter block would reload it from memory every tile).
-    const int len0 = p.ks_len[0], len1 = p.ks_len[1];
-    const int pos0 = p.ks_pos0[0], pos1 = p.ks_pos0[1];
-    const int mk0 = mk[0], mk1 = mk[1];
-    const int tlo0 = rng[0].t_lo, tlo1 = rng[1].t_lo;
+    // One descriptor per segment over this KV head's rows of that segment; a
+    // tile is addressed by its byte offset in the span (rows past the segment
+    // read as zero, kDeadTile past the last tile loads nothing).
     const int64_t head_off = (int64_t)kvh * D;
-    const uint16_t* const kseg0 = p.k + (int64_t)p.ks_row0[0] * p.hkv * D + head_off;
-    const uint16_t* const kseg1 = p.k + (int64_t)p.ks_row0[1] * p.hkv * D + head_off;
-    const uint16_t* const vseg0 = p.v + (int64_t)p.ks_row0[0] * p.hkv * D + head_off;
-    const uint16_t* const vseg1 = p.v + (int64_t)p.ks_row0[1] * p.hkv * D + head_off;
-    const int64_t tile_elems = (int64_t)kBN * p.hkv * D;
+    const int64_t kv_stride = (int64_t)p.hkv * D;
+    const __amdgpu_buffer_rsrc_t rk0 = span_rsrc(p.k + krow0 * kv_stride + head_off, (uint32_t)(len0 * row_bytes));
+    const __amdgpu_buffer_rsrc_t rk1 = span_rsrc(p.k + krow1 * kv_stride + head_off, (uint32_t)(len1 * row_bytes));
+    const __amdgpu_buffer_rsrc_t rv0 = span_rsrc(p.v + krow0 * kv_stride + head_off, (uint32_t)(len0 * row_bytes));
+    const __amdgpu_buffer_rsrc_t rv1 = span_rsrc(p.v + krow1 * kv_stride + head_off, (uint32_t)(len1 * row_bytes));
+    const int tile_bytes = kBN * row_bytes;
+    const int toff0 = tlo0 * tile_bytes, toff1 = (tlo1 - n0) * tile_bytes;
+    const TileLanes<D, kBN, kWaves> lanes(row_bytes, wave, lane);
+    // loads of K or V tile j of the step's visit order
+    auto issue = [=](bool is_v, int j, char* dst) {
+        const bool second = j >= n0;
+        const uint32_t off = (j < n_it) ? (uint32_t)(j * tile_bytes + pick(second, toff1, toff0)) : kDeadTile;
+        const __amdgpu_buffer_rsrc_t rs = is_v ? pick(second, rv1, rv0) : pick(second, rk1, rk0);
+        load_tile_at<D, kBN, kWaves>(dst, rs, lanes, off, wave);
+    };
 
-    struct TileRef {
-        int t, len, pos, mask, seg;
+    // Tile `it` of the visit order: whether it needs the element mask, its key
+    // count, first key position and mask.  (By-value capture: a select between
+    // captured references becomes a select between addresses, which the compiler
+    // keeps in a stack table and loads with a full wait.)
+    struct TileInfo {
+        bool full;
+        int kcount, kp0, mask;
     };
-    auto tile_of = [&](int it) -> TileRef {
+    auto tile_info = [=](int it) -> TileInfo {
         const bool second = it >= n0;
-        const int t = second ? tlo1 + (it - n0) : tlo0 + it;
-        return TileRef{t, second ? len1 : len0, second ? pos1 : pos0, second ? mk1 : mk0, second ? 1 : 0};
-    };
-    // Descriptor of tile `it`; past the last tile an empty descriptor, whose
-    // loads fetch nothing and write zeros (every step issues the same loads).
-    auto rsrc_of = [&](bool is_v, int it) -> __amdgpu_buffer_rsrc_t {
-        const TileRef tr = tile_of(it);
-        const bool live = it < n_it;
-        const uint16_t* base = is_v ? (tr.seg ? vseg1 : vseg0) : (tr.seg ? kseg1 : kseg0);
-        return tile_rsrc(live ? base + tr.t * tile_elems : base, live ? min(kBN, tr.len - tr.t * kBN) : 0,
-                         row_bytes);
+        const int t = it + pick(second, tlo1 - n0, tlo0);  // tile index within its segment
+        const bool full = (unsigned)(t - pick(second, flo1, flo0)) < (unsigned)pick(second, fn1, fn0);
+        return TileInfo{full, min(kBN, pick(second, len1, len0) - t * kBN), pick(second, pos1, pos0) + t * kBN,
+                        pick(second, mk1, mk0)};
     };
 
     // per-lane parts of the operand addresses (see TileLayout and key_of_reg)
@@ -208,17 +228,17 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     const int grp = lane >> 4, jl = lane & 15;
     const int v_lane = L::off(4 * (grp >> 1) + (jl >> 2), 16 * (grp & 1) + 4 * (jl & 3));
 
-    // S^T of one tile: 64 keys x this wave's 32 queries
+    // S^T of one tile: 64 keys x this wave's 32 queries (prologue only)
     auto scores = [&](const char* kt, f32x16* sc) {
+        sc[0] = f32x16{};
+        sc[1] = f32x16{};
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-            sc[kb] = f32x16{};
+        for (int ds = 0; ds < DS; ++ds)
 #pragma unroll
-            for (int ds = 0; ds < DS; ++ds) {
+            for (int kb = 0; kb < 2; ++kb) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(kt + k_lane + L::off(32 * kb, 16 * ds));
                 sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sc[kb], 0, 0, 0);
             }
-        }
     };
 
     // At each step's barrier the loads of the last two steps may still be in
@@ -226,121 +246,191 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     constexpr int kPending = 2 * 2 * (L::NBLK / kWaves);
 
     bf16x8 pb[4];  // P of the previous tile (bf16), consumed by the next step's P V
-    // Rotated pipeline step `it` (0 <= it <= n_it):
+
+    // Element mask of tile it's scores on partial or ragged tiles: key k of the
+    // tile is visible iff lo_lim <= k <= hi_lim, tested as one unsigned range
+    // compare with the lane's 4 hl folded into the limits.
+    auto mask_tile = [&](int it, f32x16* cur) {
+        const TileInfo ti = tile_info(it);
+        if (ti.full) return;
+        int hi_lim = ti.kcount - 1;
+        int lo_lim = 0;
+        if (ti.mask != CP_MASK_FULL) {
+            hi_lim = min(hi_lim, my_pos - ti.kp0);
+            if (ti.mask == CP_MASK_DOC) lo_lim = max(0, my_lo - ti.kp0);
+        }
+        const int lo_l = lo_lim - 4 * hl;
+        const unsigned span = (unsigned)(hi_lim - lo_lim);
+        const bool none = hi_lim < lo_lim;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int key0 = row_of_reg(kb, r, 0);
+                if (none || (unsigned)(key0 - lo_l) > span) cur[kb][r] = -INFINITY;
+            }
+    };
+
+    // O^T += V^T P^T over one V tile: MFMA i = s4 * DB + db covers keys
+    // 16 s4 + 4hl + {0..3, 8..11} and output dims 32 db .. 32 db + 31.  Its A
+    // operand is two transposing reads of the row-major V tile.
+    auto v_operand = [&](lds_char* vbase, int i) -> bf16x8 {
+        lds_char* a0 = vbase + L::off(16 * (i / DB), 32 * (i % DB));
+        const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
+        const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + L::off(8, 0)));
+        const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        return __builtin_bit_cast(bf16x8, a);
+    };
+    constexpr int kPV = 4 * DB;  // MFMAs of one P V product
+
+    // Raise the reference maximum when the tile's row maximum exceeds it by more
+    // than 2^8 (in the exp2 domain), rescaling the running sum and accumulator.
+    auto update_max = [&](float mloc) {
+        const float mt2 = mloc * c2;
+        const bool raise = mt2 > m2 + 8.f;
+        if (__any(raise)) {
+            const float m2n = raise ? mt2 : m2;
+            const float alpha = (m2n == m2) ? 1.f : __builtin_amdgcn_exp2f(m2 - m2n);
+            l_run *= alpha;
+#pragma unroll
+            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+            m2 = m2n;
+        }
+    };
+
+    // Scores of the next tile (2 DS MFMAs, K from LDS read two ahead) with the
+    // exponentials, bf16 P and row sum of tile it spread over them: MFMA i is
+    // followed by elements 2i and 2i+1 of this lane's 32 scores (fma, exp, sum,
+    // one packed bf16 convert).  sched_barrier keeps each slice in this order.
+    auto scores_and_exp = [&](const char* k_read, const f32x16* cur, f32x16* nxt) {
+        lds_char* kbase = lds_base(k_read, k_lane);
+        const float nb = (m2 == -INFINITY) ? 0.f : -m2;
+        auto k_operand = [&](int i) -> bf16x8 {  // MFMA i: head-dim step i / 2, key block i % 2
+            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+                kbase + L::off(32 * (i & 1), 16 * (i >> 1)));
+        };
+        constexpr int kS = 2 * DS;
+        bf16x8 ka[3];
+        ka[0] = k_operand(0);
+        ka[1] = k_operand(1);
+        nxt[0] = f32x16{};
+        nxt[1] = f32x16{};
+        float sa = 0.f, sb = 0.f;
+        uint32_t pbits[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i + 2 < kS) {
+                ka[(i + 2) % 3] = k_operand(i + 2);
+                order_memory();
+            }
+            if (i < kS) {
+                nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf[i >> 1], nxt[i & 1], 0, 0, 0);
+                pin(nxt[i & 1]);
+            }
+            const int e = 2 * i;  // elements e, e + 1: register (e % 16) of block e / 16
+            const float x0 = __builtin_amdgcn_exp2f(fmaf(cur[e >> 4][e & 15], c2, nb));
+            const float x1 = __builtin_amdgcn_exp2f(fmaf(cur[e >> 4][(e & 15) + 1], c2, nb));
+            sa += x0;
+            sb += x1;
+            const f32x2 two = {x0, x1};
+            pbits[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
+            pin(pbits[i]);
+            pin(sa);
+            pin(sb);
+        }
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const u32x4 w = {pbits[4 * q4], pbits[4 * q4 + 1], pbits[4 * q4 + 2], pbits[4 * q4 + 3]};
+            pb[q4] = __builtin_bit_cast(bf16x8, w);
+            materialise(pb[q4]);
+        }
+        l_run += sa + sb;
+        materialise(l_run);
+    };
+
+    // Rotated pipeline step it (1 <= it < n_it):
     //   loads:  K(it+4) into the K slot freed by K(it), V(it+2) into the V slot freed by V(it-2);
-    //   PV:     O^T += V(it-1)^T P(it-1)                       (MFMA, overlaps the next part)
-    //   mask, row max and rare rescale of tile it's scores  (VALU)
-    //   scores of tile it+1 (MFMA) overlapping exp / sum / bf16 of tile it (VALU) -> P(it)
+    //   mask of tile it (partial tiles only);
+    //   O^T += V(it-1)^T P(it-1) (MFMA) interleaved with tile it's row maximum (VALU);
+    //   rare rescale;
+    //   scores of tile it+1 (MFMA) interleaved with exp / sum / bf16 of tile it (VALU) -> P(it).
     // Slots: K(j) and V(j) live in slot j mod 4, so each unrolled copy below
     // touches statically known buffers.
     auto step = [&](int it, f32x16* cur, f32x16* nxt, char* k_fill, const char* k_read, char* v_fill,
                     const char* v_read) {
-        load_tile_lds<D, kBN, kWaves>(k_fill, rsrc_of(false, it + 4), row_bytes, wave, lane);
-        load_tile_lds<D, kBN, kWaves>(v_fill, rsrc_of(true, it + 2), row_bytes, wave, lane);
-
-        if (it >= 1) {
-            // O^T += V^T P^T: step s4 covers keys 16 s4 + 4hl + {0..3, 8..11}
+        issue(false, it + 4, k_fill);
+        issue(true, it + 2, v_fill);
+        mask_tile(it, cur);
+        // P V of the previous tile (V read two MFMAs ahead) with two row-maximum
+        // steps of this tile after each MFMA
+        lds_char* vbase = lds_base(v_read, v_lane);
+        bf16x8 va[3];
+        va[0] = v_operand(vbase, 0);
+        va[1] = v_operand(vbase, 1);
+        float ma = cur[0][0], mb = cur[1][0];
 #pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4) {
-#pragma unroll
-                for (int db = 0; db < DB; ++db) {
-                    const char* a0 = v_read + v_lane + L::off(16 * s4, 32 * db);
-                    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0));
-                    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a0 + L::off(8, 0)));
-                    const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                    acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), pb[s4],
-                                                                       acc[db], 0, 0, 0);
-                }
+        for (int i = 0; i < kPV; ++i) {
+            if (i + 2 < kPV) {
+                va[(i + 2) % 3] = v_operand(vbase, i + 2);
+                order_memory();
             }
+            acc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[i / DB], acc[i % DB], 0, 0, 0);
+            pin(acc[i % DB]);
+#pragma unroll
+            for (int r = (32 * i) / kPV; r < (32 * (i + 1)) / kPV; ++r)
+                if (r % 16) {
+                    if (r < 16)
+                        ma = fmaxf(ma, cur[0][r]);
+                    else
+                        mb = fmaxf(mb, cur[1][r - 16]);
+                }
+            pin(ma);
+            pin(mb);
         }
-
-        if (it < n_it) {
-            const TileRef tr = tile_of(it);
-            // element mask on partial or ragged tiles: key k of the tile is visible
-            // iff lo_lim <= k <= hi_lim, tested as one unsigned range compare with the
-            // lane's 4 hl folded into the limits
-            const int kcount = min(kBN, tr.len - tr.t * kBN);
-            const int kp0 = tr.pos + tr.t * kBN;
-            const int m = tr.mask;
-            const bool full = key_tile_full<kBN>(m, q0, m == CP_MASK_DOC ? lo1 : 0, tr.pos, tr.len, tr.t);
-            if (!full || kcount < kBN) {
-                int hi_lim = kcount - 1;
-                int lo_lim = 0;
-                if (m != CP_MASK_FULL) {
-                    hi_lim = min(hi_lim, my_pos - kp0);
-                    if (m == CP_MASK_DOC) lo_lim = max(0, my_lo - kp0);
-                }
-                const int lo_l = lo_lim - 4 * hl;
-                const unsigned span = (unsigned)(hi_lim - lo_lim);
-                const bool none = hi_lim < lo_lim;
-#pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key0 = row_of_reg(kb, r, 0);
-                        if (none || (unsigned)(key0 - lo_l) > span) cur[kb][r] = -INFINITY;
-                    }
-            }
-
-            // row maximum; the reference maximum is raised only when it grows by more than 2^8
-            float mloc = cur[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, cur[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, cur[1][r]);
-            mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
-            const float mt2 = mloc * c2;
-            const bool raise = mt2 > m2 + 8.f;
-            if (__any(raise)) {
-                const float m2n = raise ? mt2 : m2;
-                const float alpha = (m2n == m2) ? 1.f : __builtin_amdgcn_exp2f(m2 - m2n);
-                l_run *= alpha;
-#pragma unroll
-                for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-                m2 = m2n;
-            }
-            const float nb = (m2 == -INFINITY) ? 0.f : -m2;
-
-            // scores of the next tile (its K tile is resident; unused after the last tile)
-            scores(k_read, nxt);
-
-            float part[4];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int half = 0; half < 2; ++half) {
-                    f32x8 pv;
-#pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        pv[e] = __builtin_amdgcn_exp2f(fmaf(cur[kb][8 * half + e], c2, nb));
-                    pb[2 * kb + half] = __builtin_convertvector(pv, bf16x8);
-                    part[2 * kb + half] =
-                        ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-                }
-            }
-            l_run += (part[0] + part[1]) + (part[2] + part[3]);
-        }
+        update_max(max_halves(fmaxf(ma, mb)));
+        scores_and_exp(k_read, cur, nxt);
         ring_barrier<kPending>();  // the tiles the next step reads have landed; this step's slots are free
     };
 
     f32x16 sa[2], sb[2];
     if (n_it > 0) {
-        load_tile_lds<D, kBN, kWaves>(kb0, rsrc_of(false, 0), row_bytes, wave, lane);
-        load_tile_lds<D, kBN, kWaves>(kb1, rsrc_of(false, 1), row_bytes, wave, lane);
+        issue(false, 0, kb0);
+        issue(false, 1, kb1);
         __syncthreads();
         scores(kb0, sa);
         // issue order matters for the wait counts: V0, K2, V1, K3, then two per step
-        load_tile_lds<D, kBN, kWaves>(vb0, rsrc_of(true, 0), row_bytes, wave, lane);
-        load_tile_lds<D, kBN, kWaves>(kb2, rsrc_of(false, 2), row_bytes, wave, lane);
-        load_tile_lds<D, kBN, kWaves>(vb1, rsrc_of(true, 1), row_bytes, wave, lane);
-        load_tile_lds<D, kBN, kWaves>(kb3, rsrc_of(false, 3), row_bytes, wave, lane);
-        ring_barrier<kPending>();  // K(1) and V(0) have landed; every wave has read K(0)
-        for (int it = 0; it <= n_it; it += 4) {
-            step(it, sa, sb, kb0, kb1, vb2, vb3);
-            if (it + 1 <= n_it) step(it + 1, sb, sa, kb1, kb2, vb3, vb0);
-            if (it + 2 <= n_it) step(it + 2, sa, sb, kb2, kb3, vb0, vb1);
-            if (it + 3 <= n_it) step(it + 3, sb, sa, kb3, kb0, vb1, vb2);
+        issue(true, 0, vb0);
+        issue(false, 2, kb2);
+        issue(true, 1, vb1);
+        issue(false, 3, kb3);
+        ring_barrier<kPending>();  // every wave has read K(0), so its slot can be refilled
+        // step 0: no P V yet
+        issue(false, 4, kb0);
+        issue(true, 2, vb2);
+        mask_tile(0, sa);
+        {
+            float mloc = sa[0][0];
+#pragma unroll
+            for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sa[0][r]);
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sa[1][r]);
+            update_max(max_halves(mloc));
         }
+        scores_and_exp(kb1, sa, sb);
+        ring_barrier<kPending>();
+        for (int it = 1; it < n_it; it += 4) {
+            step(it, sb, sa, kb1, kb2, vb3, vb0);
+            if (it + 1 < n_it) step(it + 1, sa, sb, kb2, kb3, vb0, vb1);
+            if (it + 2 < n_it) step(it + 2, sb, sa, kb3, kb0, vb1, vb2);
+            if (it + 3 < n_it) step(it + 3, sa, sb, kb0, kb1, vb2, vb3);
+        }
+        // the last P V: V(n_it - 1) landed at the last step's barrier
+        const int last = (n_it - 1) & 3;
+        lds_char* v_last = lds_base((last == 0) ? vb0 : (last == 1) ? vb1 : (last == 2) ? vb2 : vb3, v_lane);
+#pragma unroll
+        for (int i = 0; i < kPV; ++i)
+            acc[i % DB] =
+                __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(v_last, i), pb[i / DB], acc[i % DB], 0, 0, 0);
     }
 
     // ---- epilogue: normalise, write O (fp32) and LSE (natural log)
@@ -421,6 +511,7 @@ extern "C" cp_status cp_attn_fwd_step(const cp_attn_problem* p, const void* q, c
     if (!q || !o_step || !lse_step) return fail(CP_ERR_INVALID_ARG, "NULL tensor pointer");
     if (nk > 0 && (!k || !v)) return fail(CP_ERR_INVALID_ARG, "NULL K/V pointer");
     if (n_work > (int64_t(1) << 30)) return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
+    if (!kv_spans_fit(p)) return fail(CP_ERR_UNSUPPORTED, "a KV segment spans 1 GiB or more");
     prm.n_work = int32_t(n_work);
     const int grid = int(ceil_div(n_work, 8) * 8);
     hipError_t e;

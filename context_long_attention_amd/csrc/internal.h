@@ -36,6 +36,16 @@ cp_status validate_problem(const cp_attn_problem* p, bool device_docs);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// The step kernels address a KV tile by a 32-bit byte offset into a buffer
+// descriptor spanning one segment of one KV head, so every KV segment must
+// stay below 1 GiB (len * Hkv * D * 2 bytes), leaving headroom for the offsets
+// of tiles past the end.
+inline bool kv_spans_fit(const cp_attn_problem* p) {
+    for (int j = 0; j < p->n_kv_seg; ++j)
+        if (p->kv_seg[j].len * int64_t(p->hkv) * p->head_dim * 2 >= (int64_t(1) << 30)) return false;
+    return true;
+}
+
 // Tile-range rule shared by the host block map and (as a mirror in device
 // code) the forward kernel.  For a query tile [q0, q1] (global positions, q1
 // the last row) and a KV segment starting at kpos0 with klen keys in tiles of
