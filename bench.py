@@ -2,18 +2,20 @@
 
 A step is one pass of the whole hot path for one rank: the zigzag partition and
 block classes (host), then every ring step's forward kernel with the merge of
-its partial output, with each visiting KV block staged through a receive
-buffer on a side stream.  Default workload: Llama-3-8B attention shape
+its partial output (step 0 writes the accumulator, later steps merge into it
+inside the kernel), with each visiting KV block staged through a receive buffer
+on a side stream.  Default workload: Llama-3-8B attention shape
 (Hq=32, Hkv=8, D=128, bf16) on rank 0's share of S=128K at CP=8 (local 16K
 tokens as two zigzag 8K chunks, 8 ring steps).  Inputs are seeded synthetic
 N(0,1) values rounded to bf16, resident in HBM before timing starts.
 
 Prints one JSON line.  FLOPs are causal-counted: 4*D per visible (query, key)
-pair and query head for the forward.  The roofline object's ``traffic`` is the
-HBM traffic per launch of the forward kernel from the committed FETCH_SIZE /
-WRITE_SIZE summary under profiles/, when that summary was taken on the current
-kernel sources (else null); ``--calibrate-copy-mib`` makes the known-size
-copies that summary is scaled by.
+pair and query head for the forward.  The roofline object describes the
+merging step kernel (ring steps 1..R-1); its ``traffic`` is that kernel's HBM
+traffic per launch from the committed FETCH_SIZE / WRITE_SIZE summary under
+profiles/, when that summary was taken on the current kernel sources (else
+null); ``--calibrate-copy-mib`` makes the known-size copies that summary is
+scaled by.
 """
 from __future__ import annotations
 
@@ -78,6 +80,9 @@ class KernelTimer:
     def total_ms(self):
         return sum(a.elapsed_time(b) for a, b in self.pairs)
 
+    def launch_ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
 
 def cpu_baseline(w, rank, heads):
     """The float64 oracle on a bounded sample: ``heads`` query heads of the GQA group
@@ -113,14 +118,24 @@ def cpu_baseline(w, rank, heads):
             "seconds": dt, "flops": flops}
 
 
-def fwd_algorithmic_bytes(w):
-    """Bytes one forward step launch must move at least: Q, K and V read once (bf16),
-    the step's O (fp32) and LSE (fp32) written once."""
+def fwd_algorithmic_bytes(w, live_rows, merge):
+    """Bytes one forward step launch must move at least: Q, K and V read once
+    (bf16); then for the rows that see a key in the step, O and LSE (fp32)
+    written once, or, when the launch merges into the accumulator, read and
+    written once."""
     q = w.local * w.hq * w.dim * 2
     kv = 2 * w.local * w.hkv * w.dim * 2
-    o = w.local * w.hq * w.dim * 4
-    lse = w.hq * w.local * 4
-    return q + kv + o + lse
+    out = live_rows * w.hq * (w.dim + 1) * 4
+    return q + kv + out * (2 if merge else 1)
+
+
+def live_rows(w, rank, step):
+    """Local rows with a visible key at this step of a causal ring: every row of
+    a query chunk whose chunk pairs are not all SKIP (a causal DIAG or FULL
+    pair gives each of its rows at least one key)."""
+    from context_long_attention_amd import cpattn
+    m = cpattn.cp_step_masks(w.cp, rank, step, False)
+    return w.chunk * sum(any(c != cpattn.CP_MASK_SKIP for c in row) for row in m)
 
 
 def calibration_copies(torch, mib, count=3):
@@ -183,8 +198,16 @@ def measure(torch, w, rank, steps, warmup, backward):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    per_step = [ring.step_pairs(t) * w.hq * w.dim * 4 for t in range(w.cp)]
+    launch = fwd_timer.launch_ms()
+    merge_ms = [x for i, x in enumerate(launch) if i % w.cp > 0]
     out = {"ms": ms, "fwd_kernel_ms": fwd_timer.total_ms() / steps, "flops_fwd": flops_fwd,
-           "flops_bwd": flops_bwd if backward else 0, "launches": w.cp}
+           "flops_bwd": flops_bwd if backward else 0, "launches": w.cp,
+           # the launches that merge into the accumulator (ring steps 1..R-1)
+           "merge_flops_per_launch": sum(per_step[1:]) / max(1, w.cp - 1),
+           "merge_avg_launch_ms": sum(merge_ms) / max(1, len(merge_ms)),
+           "merge_bytes_per_launch": sum(fwd_algorithmic_bytes(w, live_rows(w, rank, t), True)
+                                         for t in range(1, w.cp)) / max(1, w.cp - 1)}
     if backward:
         out["bwd_kernel_ms"] = bwd_timer.total_ms() / steps
     log(f"{w.name}: {steps} steps, {ms:.3f} ms/step, fwd kernels {out['fwd_kernel_ms']:.3f} ms"
@@ -233,8 +256,11 @@ def main():
     log(f"workload {w.name}: S={w.seq_len} CP={w.cp} Hq={w.hq} Hkv={w.hkv} D={w.dim} rank={args.rank}")
     fwd = measure(torch, w, args.rank, args.steps, args.warmup, backward=False)
     value = tflops(fwd["flops_fwd"], fwd["ms"])
-    achieved = tflops(fwd["flops_fwd"], fwd["fwd_kernel_ms"])
-    kernel = f"fwd_step_kernel<{w.dim}, {_hpw(w)}>"
+    kernel_tflops = tflops(fwd["flops_fwd"], fwd["fwd_kernel_ms"])
+    # roofline of the dominant kernel: the step kernel that merges into the
+    # accumulator (ring steps 1..R-1; step 0 writes the accumulator directly)
+    achieved = tflops(fwd["merge_flops_per_launch"], fwd["merge_avg_launch_ms"])
+    kernel = f"fwd_step_kernel<{w.dim}, {_hpw(w)}, true>"
     prof = os.path.join(ROOT, "profiles", f"fwd_step_kernel_{w.name}_traffic.md")
     measured = profsum.read_traffic(prof, kernel, w.name)
     record = {
@@ -254,16 +280,17 @@ def main():
                    "local_tokens": w.local, "hq": w.hq, "hkv": w.hkv, "head_dim": w.dim,
                    "ring_steps": w.cp, "pass": "fwd"},
         "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
-        "kernel_only": {"tflops": round(achieved, 2), "pct_bf16_peak": round(100 * achieved / BF16_PEAK_TFLOPS, 2),
+        "kernel_only": {"tflops": round(kernel_tflops, 2),
+                        "pct_bf16_peak": round(100 * kernel_tflops / BF16_PEAK_TFLOPS, 2),
                         "ms_per_step": round(fwd["fwd_kernel_ms"], 4)},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
                      "traffic": measured["traffic_bytes_per_launch"] if measured else None,
                      "kernel": kernel,
-                     "flops_per_launch": fwd["flops_fwd"] / fwd["launches"],
-                     "algorithmic_bytes_per_launch": fwd_algorithmic_bytes(w),
+                     "flops_per_launch": fwd["merge_flops_per_launch"],
+                     "algorithmic_bytes_per_launch": round(fwd["merge_bytes_per_launch"]),
                      "traffic_source": os.path.relpath(prof, ROOT) if measured else None,
-                     "avg_launch_ms": round(fwd["fwd_kernel_ms"] / fwd["launches"], 4)},
+                     "avg_launch_ms": round(fwd["merge_avg_launch_ms"], 4)},
     }
     if not args.no_bwd:
         wb = inputs.WORKLOADS[args.bwd_workload]

@@ -24,7 +24,7 @@ CP_TILE_SKIP, CP_TILE_PARTIAL, CP_TILE_FULL = 0, 1, 2
 EXPORTS = (
     "cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition_zigzag", "cp_ring_source",
     "cp_step_masks", "cp_tile_shape", "cp_block_map_size", "cp_block_map", "cp_count_pairs",
-    "cp_attn_fwd_step", "cp_merge_partials", "cp_attn_bwd_prep", "cp_attn_bwd_step",
+    "cp_attn_fwd_step", "cp_merge_partials", "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step",
 )
 
 
@@ -76,6 +76,7 @@ def lib():
             "cp_count_pairs": ([P, vp], i32),
             "cp_attn_fwd_step": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
             "cp_merge_partials": ([f32p, f32p, f32p, f32p, i64, i32, i32, vp], i32),
+            "cp_attn_fwd_step_merge": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
             "cp_attn_bwd_prep": ([vp, f32p, f32p, i64, i32, i32, vp], i32),
             "cp_attn_bwd_step": ([P, vp, vp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp], i32),
         }
@@ -187,6 +188,11 @@ def cp_attn_fwd_step(p: cp_attn_problem, q, k, v, o_step, lse_step, tile_map=Non
 def cp_merge_partials(o_acc, lse_acc, o_step, lse_step, rows, heads, head_dim, stream=None):
     _check(lib().cp_merge_partials(_ptr(o_acc), _ptr(lse_acc), _ptr(o_step), _ptr(lse_step), rows, heads,
                                    head_dim, _stream(stream)))
+
+
+def cp_attn_fwd_step_merge(p: cp_attn_problem, q, k, v, o_acc, lse_acc, tile_map=None, stream=None):
+    _check(lib().cp_attn_fwd_step_merge(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(lse_acc),
+                                        _ptr(tile_map), _stream(stream)))
 
 
 def cp_attn_bwd_prep(d_o, o, delta, rows, heads, head_dim, stream=None):

@@ -45,6 +45,8 @@ constexpr int kBN = 64;                    // keys per tile
 constexpr int kWaves = kFwdWaves;          // 8 waves: 2 per SIMD, one workgroup per CU
 constexpr int kThreads = 64 * kWaves;
 constexpr int kStages = 4;                 // K/V tiles in flight (LDS ring)
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 struct FwdParams {
     const uint16_t* q;
@@ -67,7 +69,9 @@ struct FwdParams {
     int32_t n_work;
 };
 
-template <int D, int HPW>
+// MERGE: instead of writing this step's (O, LSE), merge it into the running
+// accumulator held in p.o / p.lse (rows with no visible key are left as they are).
+template <int D, int HPW, bool MERGE>
 __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p) {
     using L = TileLayout<D, kBN>;
     constexpr int WPH = kWaves / HPW; // waves per head
@@ -433,41 +437,58 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
                 __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(v_last, i), pb[i / DB], acc[i % DB], 0, 0, 0);
     }
 
-    // ---- epilogue: normalise, write O (fp32) and LSE (natural log)
+    // ---- epilogue: normalise and write O (fp32) and LSE (natural log), or
+    // merge them into the accumulator: with this step's Ls and the stored La
+    // (base 2 below), L = log2(2^La + 2^Ls), O = 2^(La-L) O_acc + 2^(Ls-L) acc / l.
     const float l_tot = l_run + __shfl_xor(l_run, 32);
     if (row_valid) {
-        const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
         float* orow = p.o + ((int64_t)my_row * p.hq + head) * D;
+        float* lrow = p.lse + (int64_t)head * p.q_rows + my_row;
+        if constexpr (!MERGE) {
+            const float inv = (l_tot > 0.f) ? 1.f / l_tot : 0.f;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+            for (int db = 0; db < DB; ++db)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                f32x4 val = {acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv, acc[db][4 * i + 2] * inv,
-                             acc[db][4 * i + 3] * inv};
-                *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * hl) = val;
-            }
-        if (hl == 0) {
-            const float lse = (l_tot > 0.f) ? (m2 + __log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
-            p.lse[(int64_t)head * p.q_rows + my_row] = lse;
+                for (int i = 0; i < 4; ++i) {
+                    f32x4 val = {acc[db][4 * i] * inv, acc[db][4 * i + 1] * inv, acc[db][4 * i + 2] * inv,
+                                 acc[db][4 * i + 3] * inv};
+                    *reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * hl) = val;
+                }
+            if (hl == 0) *lrow = (l_tot > 0.f) ? (m2 + __log2f(l_tot)) * kLn2 : -INFINITY;
+        } else if (l_tot > 0.f) {
+            const float ls2 = m2 + __log2f(l_tot);
+            const float la2 = *lrow * kLog2e;  // -inf stays -inf
+            const float hi = fmaxf(la2, ls2);
+            const float l2 = hi + __log2f(1.f + __builtin_amdgcn_exp2f(-fabsf(la2 - ls2)));
+            const float wa = __builtin_amdgcn_exp2f(la2 - l2);
+            const float ws = __builtin_amdgcn_exp2f(ls2 - l2) / l_tot;
+#pragma unroll
+            for (int db = 0; db < DB; ++db)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    f32x4* ptr = reinterpret_cast<f32x4*>(orow + 32 * db + 8 * i + 4 * hl);
+                    const f32x4 old = *ptr;
+                    f32x4 val;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) val[j] = fmaf(wa, old[j], ws * acc[db][4 * i + j]);
+                    *ptr = val;
+                }
+            if (hl == 0) *lrow = l2 * kLn2;
         }
     }
 }
 
 template <int D, int HPW>
-hipError_t launch(const FwdParams& prm, int grid, hipStream_t stream) {
-    hipLaunchKernelGGL((fwd_step_kernel<D, HPW>), dim3(grid), dim3(kThreads), 0, stream, prm);
+hipError_t launch(const FwdParams& prm, int grid, bool merge, hipStream_t stream) {
+    if (merge)
+        hipLaunchKernelGGL((fwd_step_kernel<D, HPW, true>), dim3(grid), dim3(kThreads), 0, stream, prm);
+    else
+        hipLaunchKernelGGL((fwd_step_kernel<D, HPW, false>), dim3(grid), dim3(kThreads), 0, stream, prm);
     return hipGetLastError();
 }
 
-}  // namespace
-
-}  // namespace cpattn
-
-using namespace cpattn;
-
-extern "C" cp_status cp_attn_fwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v,
-                                      float* o_step, float* lse_step, uint8_t* tile_map_out,
-                                      hipStream_t stream) {
+cp_status fwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v, float* o_step,
+                           float* lse_step, uint8_t* tile_map_out, bool merge, hipStream_t stream) {
     cp_status st = validate_problem(p, true);
     if (st != CP_OK) return st;
     const TileGeom g = fwd_geom(p->hq, p->hkv);
@@ -516,12 +537,32 @@ extern "C" cp_status cp_attn_fwd_step(const cp_attn_problem* p, const void* q, c
     const int grid = int(ceil_div(n_work, 8) * 8);
     hipError_t e;
     if (p->head_dim == 128) {
-        e = (g.hpw == 4) ? launch<128, 4>(prm, grid, stream)
-                         : (g.hpw == 2 ? launch<128, 2>(prm, grid, stream) : launch<128, 1>(prm, grid, stream));
+        e = (g.hpw == 4) ? launch<128, 4>(prm, grid, merge, stream)
+                         : (g.hpw == 2 ? launch<128, 2>(prm, grid, merge, stream)
+                                       : launch<128, 1>(prm, grid, merge, stream));
     } else {
-        e = (g.hpw == 4) ? launch<64, 4>(prm, grid, stream)
-                         : (g.hpw == 2 ? launch<64, 2>(prm, grid, stream) : launch<64, 1>(prm, grid, stream));
+        e = (g.hpw == 4) ? launch<64, 4>(prm, grid, merge, stream)
+                         : (g.hpw == 2 ? launch<64, 2>(prm, grid, merge, stream)
+                                       : launch<64, 1>(prm, grid, merge, stream));
     }
     if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("fwd launch: ") + hipGetErrorString(e));
     return CP_OK;
+}
+
+}  // namespace
+
+}  // namespace cpattn
+
+using namespace cpattn;
+
+extern "C" cp_status cp_attn_fwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v,
+                                      float* o_step, float* lse_step, uint8_t* tile_map_out,
+                                      hipStream_t stream) {
+    return fwd_step(p, q, k, v, o_step, lse_step, tile_map_out, false, stream);
+}
+
+extern "C" cp_status cp_attn_fwd_step_merge(const cp_attn_problem* p, const void* q, const void* k, const void* v,
+                                            float* o_acc, float* lse_acc, uint8_t* tile_map_out,
+                                            hipStream_t stream) {
+    return fwd_step(p, q, k, v, o_acc, lse_acc, tile_map_out, true, stream);
 }

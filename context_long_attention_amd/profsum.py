@@ -18,7 +18,7 @@ Usage::
     python -m context_long_attention_amd.profsum stats --csv K_kernel_stats.csv \
         --command "<rocprofv3 command>" --out profiles/NAME.md
     python -m context_long_attention_amd.profsum traffic --fetch F.csv --write W.csv \
-        --kernel "fwd_step_kernel<128, 4>" --workload llama3_8b_fwd --copy-mib 1024 \
+        --kernel "fwd_step_kernel<128, 4, true>" --workload llama3_8b_fwd --copy-mib 1024 \
         --command "<fetch command>" --command "<write command>" --out profiles/NAME.md
 """
 from __future__ import annotations

@@ -90,37 +90,52 @@ class RankRing:
 
     # ------------------------------------------------------------- forward
     def forward(self, q, kv_of_source, stage: bool = True, keep_steps: bool = False, schedule=None,
-                timer=None):
+                timer=None, fused: bool = True):
         """Run the rank's forward ring.
 
         q: device bf16 [2c, Hq, D]; kv_of_source(src) -> (k, v) device bf16 [2c, Hkv, D].
         Returns (O fp32 [2c, Hq, D], LSE fp32 [Hq, 2c], per-step partials if keep_steps).
         ``timer`` (optional) is called as timer(step, "fwd_begin"/"fwd_end", stream).
+        fused: step 0 writes the accumulator and later steps merge into it inside the
+        kernel (cp_attn_fwd_step_merge); otherwise every step writes its partial and
+        cp_merge_partials folds it in (always so when keep_steps asks for the partials).
         """
         w = self.w
         rows = 2 * self.c
         sched = self.schedule() if schedule is None else list(schedule)
         check_schedule(self.R, sched)
         dev = self.device
-        o_acc = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
-        lse_acc = torch.full((w.hq, rows), float("-inf"), dtype=torch.float32, device=dev)
-        o_t = torch.empty_like(o_acc)
-        lse_t = torch.empty_like(lse_acc)
+        fused = fused and not keep_steps
         steps = []
         compute = torch.cuda.current_stream(dev)
+        if fused:
+            # the query segments cover every local row, so step 0 writes all of them
+            o_acc = torch.empty((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
+            lse_acc = torch.empty((w.hq, rows), dtype=torch.float32, device=dev)
+        else:
+            o_acc = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
+            lse_acc = torch.full((w.hq, rows), float("-inf"), dtype=torch.float32, device=dev)
+            o_t = torch.empty_like(o_acc)
+            lse_t = torch.empty_like(lse_acc)
         feeder = _Feeder(kv_of_source, sched, stage, dev)
         for t, src in enumerate(sched):
             k, v = feeder.get(t, compute)
             p = self.problem(t, src)
             if timer:
                 timer(t, "fwd_begin", compute)
-            cpattn.cp_attn_fwd_step(p, q, k, v, o_t, lse_t, stream=compute)
+            if not fused:
+                cpattn.cp_attn_fwd_step(p, q, k, v, o_t, lse_t, stream=compute)
+            elif t == 0:
+                cpattn.cp_attn_fwd_step(p, q, k, v, o_acc, lse_acc, stream=compute)
+            else:
+                cpattn.cp_attn_fwd_step_merge(p, q, k, v, o_acc, lse_acc, stream=compute)
             if timer:
                 timer(t, "fwd_end", compute)
             feeder.release(t, compute)
-            if keep_steps:
-                steps.append((o_t.clone(), lse_t.clone()))
-            cpattn.cp_merge_partials(o_acc, lse_acc, o_t, lse_t, rows, w.hq, w.dim, stream=compute)
+            if not fused:
+                if keep_steps:
+                    steps.append((o_t.clone(), lse_t.clone()))
+                cpattn.cp_merge_partials(o_acc, lse_acc, o_t, lse_t, rows, w.hq, w.dim, stream=compute)
         return o_acc, lse_acc, steps
 
     # ------------------------------------------------------------- backward

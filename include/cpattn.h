@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 1
+#define CPATTN_ABI_VERSION 2
 
 typedef enum cp_status {
     CP_OK = 0,
@@ -171,6 +171,21 @@ cp_status cp_attn_fwd_step(const cp_attn_problem* p, const void* q, const void* 
  *   lse_acc, lse_step device fp32 [heads, rows] */
 cp_status cp_merge_partials(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step,
                             int64_t rows, int32_t heads, int32_t head_dim, hipStream_t stream);
+
+/* Forward of one ring step fused with the merge of its partial output into the
+ * running accumulator ("... Million-Token Inference", section "Ring Attention
+ * Algorithms": the partial outputs are merged as the KV blocks circulate).
+ * Same problem, inputs, tiles and masks as cp_attn_fwd_step; the result equals
+ * cp_attn_fwd_step into temporaries followed by cp_merge_partials, up to the
+ * order of rounding.
+ *   o_acc   device fp32 [q_rows, Hq, D]   in/out: merged output so far
+ *   lse_acc device fp32 [Hq, q_rows]      in/out: merged LSE so far
+ * The accumulator must hold a valid state: (0, -inf), the output of an earlier
+ * cp_attn_fwd_step, or an earlier merge.  Rows with no visible key in this step
+ * are neither read nor written; nor are rows outside every query segment.
+ * tile_map_out as for cp_attn_fwd_step. */
+cp_status cp_attn_fwd_step_merge(const cp_attn_problem* p, const void* q, const void* k, const void* v,
+                                 float* o_acc, float* lse_acc, uint8_t* tile_map_out, hipStream_t stream);
 
 /* Backward preprocessing: delta[h, i] = sum_d dO[i, h, d] * O[i, h, d] with
  * the final merged O.  d_o device bf16 [rows, heads, D]; o device fp32

@@ -40,6 +40,11 @@ def _check_rank(w, rank, cu=None, check_steps=True, check_map=True):
     live = np.isfinite(rlse).T  # [rows, Hq]
     assert_o_close(o.cpu().numpy(), ro, f"merged O rank {rank}", live)
     assert_lse_close(lse.cpu().numpy(), rlse, f"merged LSE rank {rank}")
+    # the fused ring (merge inside the step kernel) reaches the same result
+    of, lf, _ = ring.forward(inp.q, inp.kv_of_source, stage=True, fused=True)
+    torch.cuda.synchronize()
+    assert_o_close(of.cpu().numpy(), ro, f"fused merged O rank {rank}", live)
+    assert_lse_close(lf.cpu().numpy(), rlse, f"fused merged LSE rank {rank}")
     if check_steps:
         for t, ((ot, lt), (rot, rlt)) in enumerate(zip(steps, rsteps)):
             assert_o_close(ot.cpu().numpy(), rot, f"O_t rank {rank} step {t}", np.isfinite(rlt).T)
@@ -146,6 +151,55 @@ def test_empty_and_skip_segments():
     cpattn.cp_attn_fwd_step(p, q, k, v, o, lse)
     torch.cuda.synchronize()
     assert torch.all(o == 7.0).item()
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_fused_step_merge_from_arbitrary_state(d):
+    """cp_attn_fwd_step_merge on a random valid accumulator (some rows empty, -inf)
+    equals the oracle's merge of that state with the step's partial; rows that see
+    no key in the step (documents) keep the accumulator untouched."""
+    from context_long_attention_amd import cpattn
+    hq, hkv, n, m = 8, 2, 200, 150
+    note(f"fused merge d={d}")
+    q64, q = device_bf16(inputs.chunk_normal(11, 0, n, hq, d))
+    k64, k = device_bf16(inputs.chunk_normal(12, 0, m, hkv, d))
+    v64, v = device_bf16(inputs.chunk_normal(13, 0, m, hkv, d))
+    cu = np.array([0, 950, 1100, 1150, 5000], dtype=np.int32)
+    cu_dev = torch.from_numpy(cu).cuda()
+    qpos, kpos = np.arange(1000, 1000 + n), np.arange(900, 900 + m)
+    DOC = cpattn.CP_MASK_DOC
+    p = cpattn.make_problem(hq, hkv, d, d ** -0.5, n, m, [(0, 1000, n)], [(0, 900, m)], [[DOC, DOC], [DOC, DOC]],
+                            cu_dev.data_ptr(), len(cu) - 1)
+    rng = np.random.default_rng(5)
+    o0 = rng.standard_normal((n, hq, d)).astype(np.float32)
+    l0 = (rng.standard_normal((hq, n)) * 4).astype(np.float32)
+    l0[:, ::7] = -np.inf
+    l0[2, 100:130] = 30.0  # a dominant accumulator
+    o0.transpose(1, 0, 2)[np.isneginf(l0)] = 0  # (0, -inf) is the empty state
+    o_acc = torch.from_numpy(o0.copy()).cuda()
+    l_acc = torch.from_numpy(l0.copy()).cuda()
+    cpattn.cp_attn_fwd_step_merge(p, q, k, v, o_acc, l_acc)
+    # the same through a separate partial and cp_merge_partials
+    o_sep = torch.from_numpy(o0.copy()).cuda()
+    l_sep = torch.from_numpy(l0.copy()).cuda()
+    o_t = torch.empty((n, hq, d), dtype=torch.float32, device="cuda")
+    l_t = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    cpattn.cp_attn_fwd_step(p, q, k, v, o_t, l_t)
+    cpattn.cp_merge_partials(o_sep, l_sep, o_t, l_t, n, hq, d)
+    torch.cuda.synchronize()
+    ro_t, rl_t = oracle.attention_partial(q64, k64, v64, oracle.visibility(qpos, kpos, cu), d ** -0.5)
+    ro, rl = oracle.merge(o0.astype(np.float64), l0.astype(np.float64), ro_t, rl_t)
+    assert np.isneginf(rl_t).any() and np.isfinite(rl_t).any()
+    assert_o_close(o_acc.cpu().numpy(), ro, "fused merge O")
+    assert_lse_close(l_acc.cpu().numpy(), rl, "fused merge LSE")
+    np.testing.assert_allclose(o_acc.cpu().numpy(), o_sep.cpu().numpy(), atol=2e-5, rtol=1e-5)
+    got_l, sep_l = l_acc.cpu().numpy(), l_sep.cpu().numpy()
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(sep_l))
+    np.testing.assert_allclose(got_l[np.isfinite(got_l)], sep_l[np.isfinite(sep_l)], atol=2e-5, rtol=1e-6)
+    # rows with nothing visible in this step are bit-identical to the initial state
+    dead = np.isneginf(rl_t)
+    assert np.array_equal(got_l[dead], l0[dead])
+    assert np.array_equal(o_acc.cpu().numpy().transpose(1, 0, 2)[dead], o0.transpose(1, 0, 2)[dead])
 
 
 def test_merge_kernel_matches_oracle():
