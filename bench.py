@@ -84,6 +84,62 @@ class KernelTimer:
         return [a.elapsed_time(b) for a, b in self.pairs]
 
 
+class ClockSampler:
+    """GFX clock (MHz) and socket power (W) as reported by amd-smi, sampled every
+    `period` seconds in a background thread while a measured leg runs (warm-up
+    and timed steps; the driver's own sampling window may be coarser).  Reads
+    only; reports None where amd-smi is unavailable."""
+
+    def __init__(self, period=0.02):
+        import threading
+        self.period = period
+        self.clk, self.power = [], []
+        self._stop = threading.Event()
+        self._thread = None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi
+            self.handle = amdsmi.amdsmi_get_processor_handles()[0]  # the box's one GPU
+        except Exception:  # noqa: BLE001 -- any failure just disables the readings
+            self.smi = self.handle = None
+
+    def _sample(self):
+        a = self.smi
+        while not self._stop.is_set():
+            try:
+                c = a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)
+                v = c.get("clk", c.get("cur_clk"))
+                if isinstance(v, (int, float)) and v > 0:
+                    self.clk.append(float(v))
+                pw = a.amdsmi_get_power_info(self.handle)
+                v = pw.get("current_socket_power", pw.get("average_socket_power"))
+                if isinstance(v, (int, float)) and v > 0:
+                    self.power.append(float(v))
+            except Exception:  # noqa: BLE001
+                pass
+            self._stop.wait(self.period)
+
+    def start(self):
+        import threading
+        if self.handle is not None:
+            self._thread = threading.Thread(target=self._sample, daemon=True)
+            self._thread.start()
+        return self
+
+    def stop(self):
+        if self._thread is None:
+            return None
+        self._stop.set()
+        self._thread.join()
+        if not self.clk:
+            return None
+        med = lambda x: float(np.median(x)) if x else None
+        return {"sclk_mhz_median": med(self.clk), "sclk_mhz_min": min(self.clk), "sclk_mhz_max": max(self.clk),
+                "socket_power_w_median": med(self.power), "samples": len(self.clk),
+                "source": "amd-smi GFX clock / socket power, sampled every 20 ms over warm-up and timed steps"}
+
+
 def cpu_baseline(w, rank, heads):
     """The float64 oracle on a bounded sample: ``heads`` query heads of the GQA group
     of KV head 0, every ring step of the rank, every local row."""
@@ -184,6 +240,7 @@ def measure(torch, w, rank, steps, warmup, backward):
         if backward:
             r.backward(q, d_o, o, lse, kv_of, stage=True, keep_steps=False, timer=timer)
 
+    sampler = ClockSampler().start()
     for i in range(warmup):
         one_step()
         torch.cuda.synchronize()
@@ -198,11 +255,12 @@ def measure(torch, w, rank, steps, warmup, backward):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    clocks = sampler.stop()
     per_step = [ring.step_pairs(t) * w.hq * w.dim * 4 for t in range(w.cp)]
     launch = fwd_timer.launch_ms()
     merge_ms = [x for i, x in enumerate(launch) if i % w.cp > 0]
     out = {"ms": ms, "fwd_kernel_ms": fwd_timer.total_ms() / steps, "flops_fwd": flops_fwd,
-           "flops_bwd": flops_bwd if backward else 0, "launches": w.cp,
+           "flops_bwd": flops_bwd if backward else 0, "launches": w.cp, "clocks": clocks,
            # the launches that merge into the accumulator (ring steps 1..R-1)
            "merge_flops_per_launch": sum(per_step[1:]) / max(1, w.cp - 1),
            "merge_avg_launch_ms": sum(merge_ms) / max(1, len(merge_ms)),
@@ -280,6 +338,7 @@ def main():
                    "local_tokens": w.local, "hq": w.hq, "hkv": w.hkv, "head_dim": w.dim,
                    "ring_steps": w.cp, "pass": "fwd"},
         "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "clocks": fwd["clocks"],
         "kernel_only": {"tflops": round(kernel_tflops, 2),
                         "pct_bf16_peak": round(100 * kernel_tflops / BF16_PEAK_TFLOPS, 2),
                         "ms_per_step": round(fwd["fwd_kernel_ms"], 4)},
@@ -304,6 +363,7 @@ def main():
             "fwd_kernel_tflops": round(tflops(fb["flops_fwd"], fb["fwd_kernel_ms"]), 2),
             "bwd_kernel_tflops": round(tflops(fb["flops_bwd"], fb["bwd_kernel_ms"]), 2),
             "bwd_kernel_ms_per_step": round(fb["bwd_kernel_ms"], 4),
+            "clocks": fb["clocks"],
         }
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host (cpu_baseline)")
