@@ -84,60 +84,35 @@ class KernelTimer:
         return [a.elapsed_time(b) for a, b in self.pairs]
 
 
-class ClockSampler:
-    """GFX clock (MHz) and socket power (W) as reported by amd-smi, sampled every
-    `period` seconds in a background thread while a measured leg runs (warm-up
-    and timed steps; the driver's own sampling window may be coarser).  Reads
-    only; reports None where amd-smi is unavailable."""
-
-    def __init__(self, period=0.02):
-        import threading
-        self.period = period
-        self.clk, self.power = [], []
-        self._stop = threading.Event()
-        self._thread = None
-        try:
-            import amdsmi
-            amdsmi.amdsmi_init()
-            self.smi = amdsmi
-            self.handle = amdsmi.amdsmi_get_processor_handles()[0]  # the box's one GPU
-        except Exception:  # noqa: BLE001 -- any failure just disables the readings
-            self.smi = self.handle = None
-
-    def _sample(self):
-        a = self.smi
-        while not self._stop.is_set():
-            try:
-                c = a.amdsmi_get_clock_info(self.handle, a.AmdSmiClkType.GFX)
-                v = c.get("clk", c.get("cur_clk"))
-                if isinstance(v, (int, float)) and v > 0:
-                    self.clk.append(float(v))
-                pw = a.amdsmi_get_power_info(self.handle)
-                v = pw.get("current_socket_power", pw.get("average_socket_power"))
-                if isinstance(v, (int, float)) and v > 0:
-                    self.power.append(float(v))
-            except Exception:  # noqa: BLE001
-                pass
-            self._stop.wait(self.period)
-
-    def start(self):
-        import threading
-        if self.handle is not None:
-            self._thread = threading.Thread(target=self._sample, daemon=True)
-            self._thread.start()
-        return self
-
-    def stop(self):
-        if self._thread is None:
-            return None
-        self._stop.set()
-        self._thread.join()
-        if not self.clk:
-            return None
-        med = lambda x: float(np.median(x)) if x else None
-        return {"sclk_mhz_median": med(self.clk), "sclk_mhz_min": min(self.clk), "sclk_mhz_max": max(self.clk),
-                "socket_power_w_median": med(self.power), "samples": len(self.clk),
-                "source": "amd-smi GFX clock / socket power, sampled every 20 ms over warm-up and timed steps"}
+def probe_clock(torch, one_step):
+    """Shader clock the forward step kernel runs at, from its own counters: one
+    extra (untimed) pass with cp_debug_clock_probe on; per workgroup of the pass's
+    last launch, clock = cycle-counter difference / 100 MHz tick difference.
+    Workgroups shorter than 10 us (steps where their tile sees no key) are left
+    out.  Returns the median over workgroups and per XCD (workgroup id mod 8)."""
+    from context_long_attention_amd import cpattn
+    buf = torch.zeros(4 * 65536, dtype=torch.int64, device="cuda")
+    cpattn.cp_debug_clock_probe(buf)
+    try:
+        one_step()
+        torch.cuda.synchronize()
+    finally:
+        cpattn.cp_debug_clock_probe(None)
+    rec = buf.view(-1, 4).cpu().numpy()
+    ids = np.nonzero(rec[:, 1])[0]
+    rec = rec[ids]
+    ticks = rec[:, 3] - rec[:, 1]
+    keep = ticks >= 1000
+    if not keep.any():
+        return None
+    mhz = (rec[keep, 2] - rec[keep, 0]) / ticks[keep] * 100.0
+    xcd = ids[keep] % 8
+    return {"sclk_mhz_median": round(float(np.median(mhz)), 1),
+            "sclk_mhz_per_xcd": [round(float(np.median(mhz[xcd == x])), 1) if (xcd == x).any() else None
+                                 for x in range(8)],
+            "workgroups": int(keep.sum()),
+            "source": "forward step kernel's own cycle / 100 MHz counters (cp_debug_clock_probe), last launch "
+                      "of an extra untimed pass"}
 
 
 def cpu_baseline(w, rank, heads):
@@ -240,7 +215,6 @@ def measure(torch, w, rank, steps, warmup, backward):
         if backward:
             r.backward(q, d_o, o, lse, kv_of, stage=True, keep_steps=False, timer=timer)
 
-    sampler = ClockSampler().start()
     for i in range(warmup):
         one_step()
         torch.cuda.synchronize()
@@ -255,7 +229,8 @@ def measure(torch, w, rank, steps, warmup, backward):
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
-    clocks = sampler.stop()
+    fwd_timer.enabled = bwd_timer.enabled = False
+    clocks = probe_clock(torch, one_step)
     per_step = [ring.step_pairs(t) * w.hq * w.dim * 4 for t in range(w.cp)]
     launch = fwd_timer.launch_ms()
     merge_ms = [x for i, x in enumerate(launch) if i % w.cp > 0]
@@ -280,6 +255,97 @@ def _hpw(w):
     return 256 // bm
 
 
+def _dev_normal(torch, shape, seed):
+    """Seeded N(0,1) draws made on the device and rounded to bf16 (the variant legs;
+    the shapes, not the values, matter for timing)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    return torch.randn(shape, generator=g, device="cuda", dtype=torch.float32).to(torch.bfloat16)
+
+
+def _time_leg(torch, fn, steps, warmup, timer=None):
+    """(ms per call of fn over `steps` timed calls, kernel ms per call or None)."""
+    for _ in range(warmup):
+        fn(None)
+    torch.cuda.synchronize()
+    if timer is not None:
+        timer.enabled = True
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn(timer)
+    b.record()
+    torch.cuda.synchronize()
+    kern = timer.total_ms() / steps if timer is not None else None
+    return a.elapsed_time(b) / steps, kern
+
+
+def measure_variants(torch, w, rank, steps, warmup):
+    """The ring variants beside Pass KV, at the Llama-3-8B forward shape."""
+    from context_long_attention_amd import cpattn
+    from context_long_attention_amd.variants import (PartialPrefillRank, PassQRank, gathered_forward,
+                                                     head_sharded_forward)
+    out = {}
+    c, R = w.chunk, w.cp
+    fpp = w.hq * w.dim * 4  # forward FLOP per visible pair (all query heads)
+
+    # Pass Q: the rank's K/V stay, every rank's Q block visits; then the owner's
+    # merge of the R partials it receives (the rank's own partials stand in for them)
+    pq = PassQRank(w, rank)
+    k = _dev_normal(torch, (2 * c, w.hkv, w.dim), 101)
+    v = _dev_normal(torch, (2 * c, w.hkv, w.dim), 102)
+    qs = {s: _dev_normal(torch, (2 * c, w.hq, w.dim), 200 + s) for s in range(R)}
+    pairs = sum(cpattn.cp_count_pairs(pq.problem(t)) for t in range(R))
+
+    def pass_q(timer):
+        parts = pq.forward(k, v, qs.__getitem__, stage=True, timer=timer)
+        pq.restore([(o, l) for _, o, l in parts])
+
+    ms, kern = _time_leg(torch, pass_q, steps, warmup, KernelTimer(torch, "fwd"))
+    out["pass_q"] = {"workload": f"{w.name} Pass Q rank {rank}", "tflops": round(tflops(pairs * fpp, ms), 2),
+                     "kernel_tflops": round(tflops(pairs * fpp, kern), 2), "ms_per_step": round(ms, 4)}
+    del qs
+    log(f"pass_q: {ms:.3f} ms/step")
+
+    # partial prefill: 96K cached + 32K new tokens over CP=8
+    P, N = 3 * w.seq_len // 4, w.seq_len // 4
+    pp = PartialPrefillRank(P, N, R, w.hq, w.hkv, w.dim, rank)
+    q_new = _dev_normal(torch, (2 * pp.cn, w.hq, w.dim), 301)
+    kvs = {s: (_dev_normal(torch, (2 * pp.cc, w.hkv, w.dim), 400 + s), _dev_normal(torch, (2 * pp.cc, w.hkv, w.dim), 500 + s),
+               _dev_normal(torch, (2 * pp.cn, w.hkv, w.dim), 600 + s), _dev_normal(torch, (2 * pp.cn, w.hkv, w.dim), 700 + s))
+           for s in range(R)}
+    pairs = sum(cpattn.cp_count_pairs(p) for t in range(R) for p in pp.problems(t))
+    ms, kern = _time_leg(torch, lambda timer: pp.forward(q_new, kvs.__getitem__, stage=True, timer=timer), steps,
+                         warmup, KernelTimer(torch, "fwd"))
+    out["partial_prefill"] = {"workload": f"Llama-3-8B partial prefill, {P} cached + {N} new tokens, CP={R}, rank {rank}",
+                              "tflops": round(tflops(pairs * fpp, ms), 2),
+                              "kernel_tflops": round(tflops(pairs * fpp, kern), 2), "ms_per_step": round(ms, 4)}
+    del kvs
+    log(f"partial_prefill: {ms:.3f} ms/step")
+
+    # gathered KV (all-gather strategy): the rank's query share against the whole sequence
+    q_loc = _dev_normal(torch, (2 * c, w.hq, w.dim), 801)
+    k_all = _dev_normal(torch, (w.seq_len, w.hkv, w.dim), 802)
+    v_all = _dev_normal(torch, (w.seq_len, w.hkv, w.dim), 803)
+    ring_pairs = 2 * R * c * c + c
+    ms, _ = _time_leg(torch, lambda timer: gathered_forward(w, rank, q_loc, k_all, v_all), steps, warmup)
+    out["all_gather"] = {"workload": f"{w.name} gathered KV, rank {rank}", "tflops": round(tflops(ring_pairs * fpp, ms), 2),
+                         "ms_per_step": round(ms, 4)}
+    log(f"all_gather: {ms:.3f} ms/step")
+
+    # head-sharded (all-to-all strategy): the whole sequence for Hq/R and Hkv/R heads
+    hq_d, hkv_d = w.hq // R, max(1, w.hkv // R)
+    q_h = _dev_normal(torch, (w.seq_len, hq_d, w.dim), 901)
+    k_h = _dev_normal(torch, (w.seq_len, hkv_d, w.dim), 902)
+    v_h = _dev_normal(torch, (w.seq_len, hkv_d, w.dim), 903)
+    pairs = w.seq_len * (w.seq_len + 1) // 2
+    ms, _ = _time_leg(torch, lambda timer: head_sharded_forward(q_h, k_h, v_h, w.scale), steps, warmup)
+    out["ulysses"] = {"workload": f"{w.name} head-sharded, {hq_d} query heads / {hkv_d} KV head over {w.seq_len} tokens",
+                      "tflops": round(tflops(pairs * hq_d * w.dim * 4, ms), 2), "ms_per_step": round(ms, 4)}
+    log(f"ulysses: {ms:.3f} ms/step")
+    return out
+
+
 def tflops(flops, ms):
     return flops / (ms * 1e-3) / 1e12
 
@@ -295,6 +361,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
+    ap.add_argument("--no-variants", action="store_true", help="skip the Pass Q / prefill / gathered legs")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first make 3 device-to-device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -365,6 +432,8 @@ def main():
             "bwd_kernel_ms_per_step": round(fb["bwd_kernel_ms"], 4),
             "clocks": fb["clocks"],
         }
+    if not args.no_variants:
+        record["variants"] = measure_variants(torch, w, args.rank, max(1, args.steps // 2), 1)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host (cpu_baseline)")
         record["cpu_baseline"] = cpu_baseline(w, args.rank, args.cpu_heads)

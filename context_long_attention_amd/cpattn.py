@@ -25,6 +25,7 @@ EXPORTS = (
     "cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition_zigzag", "cp_ring_source",
     "cp_step_masks", "cp_tile_shape", "cp_block_map_size", "cp_block_map", "cp_count_pairs",
     "cp_attn_fwd_step", "cp_merge_partials", "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step",
+    "cp_debug_clock_probe",
 )
 
 
@@ -77,6 +78,7 @@ def lib():
             "cp_attn_fwd_step": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
             "cp_merge_partials": ([f32p, f32p, f32p, f32p, i64, i32, i32, vp], i32),
             "cp_attn_fwd_step_merge": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
+            "cp_debug_clock_probe": ([vp, i64], i32),
             "cp_attn_bwd_prep": ([vp, f32p, f32p, i64, i32, i32, vp], i32),
             "cp_attn_bwd_step": ([P, vp, vp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp], i32),
         }
@@ -193,6 +195,12 @@ def cp_merge_partials(o_acc, lse_acc, o_step, lse_step, rows, heads, head_dim, s
 def cp_attn_fwd_step_merge(p: cp_attn_problem, q, k, v, o_acc, lse_acc, tile_map=None, stream=None):
     _check(lib().cp_attn_fwd_step_merge(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(lse_acc),
                                         _ptr(tile_map), _stream(stream)))
+
+
+def cp_debug_clock_probe(buf=None):
+    """Record per-workgroup (cycles, 100 MHz ticks) at start and end of every forward
+    step launch into ``buf`` (device int64 tensor, 4 values per workgroup); None stops."""
+    _check(lib().cp_debug_clock_probe(_ptr(buf), 0 if buf is None else buf.numel()))
 
 
 def cp_attn_bwd_prep(d_o, o, delta, rows, heads, head_dim, stream=None):

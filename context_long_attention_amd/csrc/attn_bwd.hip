@@ -61,7 +61,7 @@ struct BwdParams {
     // dK/dV kernel: 128-key tiles
     int32_t ktiles0, n_ktiles, n_work_kv;
     // dQ kernel: query tiles of BMQ rows
-    int32_t qtiles0, n_qtiles, n_work_q;
+    int32_t qtiles0, n_qtiles, n_work_q, n_hb;
 };
 
 // ============================================================================ dK / dV
@@ -99,11 +99,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     const int hl = lane >> 5;
     const int ql = lane & 31;
 
-    const int per_xcd = gridDim.x >> 3;
-    const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    // item w runs on XCD w mod 8 (workgroups are dealt round-robin): KV head
+    // w mod Hkv, key tiles earliest first (the most queries)
+    const int w = blockIdx.x;
     if (w >= p.n_work_kv) return;
-    const int g = w / p.n_ktiles;
-    const int kt = w % p.n_ktiles;
+    const int g = w % p.hkv;
+    const int kt = w / p.hkv;
     const int s = (kt < p.ktiles0) ? 0 : 1;
     const int kt_in = s ? kt - p.ktiles0 : kt;
     const int key_row0 = p.ks_row0[s] + kt_in * BK;
@@ -344,11 +345,11 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
     const int hl = lane >> 5;
     const int ql = lane & 31;
 
-    const int per_xcd = gridDim.x >> 3;
-    const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    // as in the forward: head block w mod n_hb, query tiles latest first
+    const int w = blockIdx.x;
     if (w >= p.n_work_q) return;
-    const int hb = w / p.n_qtiles;
-    const int qt = p.n_qtiles - 1 - (w % p.n_qtiles);
+    const int hb = w % p.n_hb;
+    const int qt = p.n_qtiles - 1 - w / p.n_hb;
     const int qs = (qt < p.qtiles0) ? 0 : 1;
     const int qt_in = qs ? qt - p.qtiles0 : qt;
     const int tile_row0 = p.qs_row0[qs] + qt_in * BMQ;
@@ -621,14 +622,15 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
         return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     prm.n_work_kv = int32_t(work_kv);
     prm.n_work_q = int32_t(work_q);
+    prm.n_hb = p->hq / gq.hpw;
     hipError_t e = hipSuccess;
     if (work_kv > 0) {
-        const int grid = int(ceil_div(work_kv, 8) * 8);
+        const int grid = int(work_kv);
         e = (p->head_dim == 128) ? launch_dkdv<128>(prm, grid, stream) : launch_dkdv<64>(prm, grid, stream);
         if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd dK/dV launch: ") + hipGetErrorString(e));
     }
     if (work_q > 0) {
-        const int grid = int(ceil_div(work_q, 8) * 8);
+        const int grid = int(work_q);
         if (p->head_dim == 128)
             e = (gq.hpw == 4) ? launch_dq<128, 4>(prm, grid, stream)
                               : (gq.hpw == 2 ? launch_dq<128, 2>(prm, grid, stream) : launch_dq<128, 1>(prm, grid, stream));

@@ -25,10 +25,13 @@
 //    then bounded by 256, which fp32 accumulation and bf16 rounding absorb.
 //  * Tiles with no visible pair are never visited (block-sparse skip); the
 //    element mask runs only on partially visible or ragged tiles.
-//  * Workgroup ids map each XCD (ids equal mod 8) to one range of head blocks
-//    (K/V shared in its L2), latest query positions first.
+//  * Work items are dealt to the XCDs round-robin: each XCD keeps the same head
+//    blocks (K/V shared in its L2), latest query positions first, and query
+//    tiles of a head block shared by several XCDs interleave across them.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -66,7 +69,9 @@ struct FwdParams {
     int32_t mask[2][2];
     int32_t qtiles0, n_qtiles;
     int32_t ktiles0, n_ktiles;
-    int32_t n_work;
+    int32_t n_work, n_hb;
+    unsigned long long* clk;  // diagnostics: per-workgroup start/end counters, or null
+    int32_t clk_wgs;
 };
 
 // MERGE: instead of writing this step's (O, LSE), merge it into the running
@@ -97,12 +102,20 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     const int hl = lane >> 5;
     const int ql = lane & 31;
 
-    // ---- work decode: XCD-major ranges of head blocks, latest query tiles first
-    const int per_xcd = gridDim.x >> 3;
-    const int w = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    // ---- work decode.  Workgroups are dealt to the 8 XCDs round-robin by id, so
+    // item w goes to XCD w mod 8: head block w mod n_hb (every XCD keeps the same
+    // head blocks, whose K/V then stay in its L2) and query tiles latest first
+    // (the most keys), interleaved across the XCDs sharing a head block.
+    const int w = blockIdx.x;
     if (w >= p.n_work) return;
-    const int hb = w / p.n_qtiles;
-    const int qt = p.n_qtiles - 1 - (w % p.n_qtiles);
+    const bool probe = p.clk != nullptr && w < p.clk_wgs;
+    unsigned long long t0_cycles = 0, t0_ticks = 0;
+    if (probe) {
+        t0_cycles = __builtin_readcyclecounter();
+        t0_ticks = __builtin_readsteadycounter();
+    }
+    const int hb = w % p.n_hb;
+    const int qt = p.n_qtiles - 1 - w / p.n_hb;
     const int qs = (qt < p.qtiles0) ? 0 : 1;
     const int qt_in = qs ? qt - p.qtiles0 : qt;
     // Segment parameters as opaque scalars; nothing below indexes the parameter
@@ -476,6 +489,13 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
             if (hl == 0) *lrow = l2 * kLn2;
         }
     }
+    if (probe && tid == 0) {
+        unsigned long long* rec = p.clk + 4 * (int64_t)w;
+        rec[0] = t0_cycles;
+        rec[1] = t0_ticks;
+        rec[2] = __builtin_readcyclecounter();
+        rec[3] = __builtin_readsteadycounter();
+    }
 }
 
 template <int D, int HPW>
@@ -486,6 +506,10 @@ hipError_t launch(const FwdParams& prm, int grid, bool merge, hipStream_t stream
         hipLaunchKernelGGL((fwd_step_kernel<D, HPW, false>), dim3(grid), dim3(kThreads), 0, stream, prm);
     return hipGetLastError();
 }
+
+// diagnostics (cp_debug_clock_probe)
+std::atomic<unsigned long long*> g_clock_buf{nullptr};
+std::atomic<int64_t> g_clock_cap{0};
 
 cp_status fwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v, float* o_step,
                            float* lse_step, uint8_t* tile_map_out, bool merge, hipStream_t stream) {
@@ -500,6 +524,8 @@ cp_status fwd_step(const cp_attn_problem* p, const void* q, const void* k, const
     prm.lse = lse_step;
     prm.cu = p->cu_seqlens;
     prm.tile_map = tile_map_out;
+    prm.clk = g_clock_buf.load();
+    prm.clk_wgs = int32_t(std::min<int64_t>(g_clock_cap.load() / 4, int64_t(1) << 30));
     prm.n_docs = p->n_docs;
     prm.hq = p->hq;
     prm.hkv = p->hkv;
@@ -534,7 +560,8 @@ cp_status fwd_step(const cp_attn_problem* p, const void* q, const void* k, const
     if (n_work > (int64_t(1) << 30)) return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     if (!kv_spans_fit(p)) return fail(CP_ERR_UNSUPPORTED, "a KV segment spans 1 GiB or more");
     prm.n_work = int32_t(n_work);
-    const int grid = int(ceil_div(n_work, 8) * 8);
+    prm.n_hb = p->hq / g.hpw;
+    const int grid = int(n_work);
     hipError_t e;
     if (p->head_dim == 128) {
         e = (g.hpw == 4) ? launch<128, 4>(prm, grid, merge, stream)
@@ -565,4 +592,11 @@ extern "C" cp_status cp_attn_fwd_step_merge(const cp_attn_problem* p, const void
                                             float* o_acc, float* lse_acc, uint8_t* tile_map_out,
                                             hipStream_t stream) {
     return fwd_step(p, q, k, v, o_acc, lse_acc, tile_map_out, true, stream);
+}
+
+extern "C" cp_status cp_debug_clock_probe(uint64_t* dev_buf, int64_t capacity) {
+    if (dev_buf && capacity < 4) return fail(CP_ERR_INVALID_ARG, "clock probe buffer holds fewer than 4 values");
+    g_clock_cap.store(dev_buf ? capacity : 0);
+    g_clock_buf.store(reinterpret_cast<unsigned long long*>(dev_buf));
+    return CP_OK;
 }

@@ -174,17 +174,31 @@ class RankRing:
         return dq, out
 
 
-class _Feeder:
-    """Supplies the KV block of each step, optionally through a double-buffered
-    receive buffer filled on a side stream (the stand-in for the ring transfer)."""
+_SIDE_STREAMS = {}
 
-    def __init__(self, kv_of_source, sched, stage, dev):
-        self.kv_of_source = kv_of_source
+
+def _side_stream(dev):
+    """One receive stream per device for the whole process.  A fresh stream per
+    ring would be taken round-robin from torch's pool and could share a hardware
+    queue with the compute stream, serialising the copies with the kernels."""
+    key = torch.device(dev).index if torch.device(dev).index is not None else torch.cuda.current_device()
+    if key not in _SIDE_STREAMS:
+        _SIDE_STREAMS[key] = torch.cuda.Stream(torch.device("cuda", key))
+    return _SIDE_STREAMS[key]
+
+
+class _Feeder:
+    """Supplies the block of each step (a tuple of tensors: (K, V) for Pass KV,
+    (Q,) for Pass Q), optionally through a double-buffered receive buffer filled
+    on a side stream (the stand-in for the ring transfer)."""
+
+    def __init__(self, block_of_source, sched, stage, dev):
+        self.block_of_source = block_of_source
         self.sched = sched
         self.stage = stage
         self.dev = dev
         if stage:
-            self.side = torch.cuda.Stream(dev)
+            self.side = _side_stream(dev)
             # The receive buffers come from torch's caching allocator, which may hand
             # back blocks whose previous users are still queued on the compute stream:
             # the first copy must not start before that earlier work.
@@ -196,25 +210,25 @@ class _Feeder:
             self._issue(0)
 
     def _issue(self, t):
-        k_src, v_src = self.kv_of_source(self.sched[t])
+        src = tuple(self.block_of_source(self.sched[t]))
         slot = t % 2
         if self.buf[slot] is None:
-            kb, vb = torch.empty_like(k_src), torch.empty_like(v_src)
-            # written on the side stream: keep the blocks until its work is done
-            kb.record_stream(self.side)
-            vb.record_stream(self.side)
-            self.buf[slot] = (kb, vb)
-        kb, vb = self.buf[slot]
+            bufs = tuple(torch.empty_like(x) for x in src)
+            for b in bufs:
+                # written on the side stream: keep the blocks until its work is done
+                b.record_stream(self.side)
+            self.buf[slot] = bufs
+        bufs = self.buf[slot]
         with torch.cuda.stream(self.side):
             if self.free_recorded[slot]:
                 self.side.wait_event(self.free[slot])
-            kb.copy_(k_src, non_blocking=True)
-            vb.copy_(v_src, non_blocking=True)
+            for b, x in zip(bufs, src):
+                b.copy_(x, non_blocking=True)
             self.ready[slot].record(self.side)
 
     def get(self, t, compute):
         if not self.stage:
-            return self.kv_of_source(self.sched[t])
+            return tuple(self.block_of_source(self.sched[t]))
         slot = t % 2
         compute.wait_event(self.ready[slot])
         if t + 1 < len(self.sched):

@@ -187,6 +187,17 @@ cp_status cp_merge_partials(float* o_acc, float* lse_acc, const float* o_step, c
 cp_status cp_attn_fwd_step_merge(const cp_attn_problem* p, const void* q, const void* k, const void* v,
                                  float* o_acc, float* lse_acc, uint8_t* tile_map_out, hipStream_t stream);
 
+/* Diagnostics, not part of the method.  While dev_buf (device memory of
+ * `capacity` uint64 values) is set, every forward step launch (cp_attn_fwd_step,
+ * cp_attn_fwd_step_merge) records, for each of its first capacity / 4
+ * workgroups b, four values at dev_buf[4b .. 4b+3]: the shader cycle counter and
+ * the constant 100 MHz counter when the workgroup starts, then the same two when
+ * it ends; the ratio of the differences gives the shader clock the work ran at.
+ * Each launch overwrites the records of its workgroups.  NULL (the default)
+ * turns recording off.  The setting is process-wide and read at launch time.
+ * Returns CP_ERR_INVALID_ARG for a non-NULL buffer with capacity < 4. */
+cp_status cp_debug_clock_probe(uint64_t* dev_buf, int64_t capacity);
+
 /* Backward preprocessing: delta[h, i] = sum_d dO[i, h, d] * O[i, h, d] with
  * the final merged O.  d_o device bf16 [rows, heads, D]; o device fp32
  * [rows, heads, D]; delta device fp32 [heads, rows] (overwritten). */

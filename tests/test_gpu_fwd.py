@@ -202,6 +202,34 @@ def test_fused_step_merge_from_arbitrary_state(d):
     assert np.array_equal(o_acc.cpu().numpy().transpose(1, 0, 2)[dead], o0.transpose(1, 0, 2)[dead])
 
 
+def test_clock_probe_records_every_workgroup():
+    """cp_debug_clock_probe: each workgroup of a launch records start/end cycle and
+    100 MHz tick counters; the implied shader clock is a plausible one."""
+    from context_long_attention_amd import cpattn
+    w = inputs.Workload("probe", 4096, 2, 8, 2, 128, backward=False)
+    inp = RankInputs(w, 0)
+    ring = _ring(w, 0)
+    p = ring.problem(0)
+    o = torch.empty((w.local, w.hq, w.dim), dtype=torch.float32, device="cuda")
+    lse = torch.empty((w.hq, w.local), dtype=torch.float32, device="cuda")
+    buf = torch.zeros(4 * 4096, dtype=torch.int64, device="cuda")
+    cpattn.cp_debug_clock_probe(buf)
+    try:
+        k, v = inp.kv_of_source(ring.schedule()[0])
+        cpattn.cp_attn_fwd_step(p, inp.q, k, v, o, lse)
+        torch.cuda.synchronize()
+    finally:
+        cpattn.cp_debug_clock_probe(None)
+    bm, _ = cpattn.cp_tile_shape(w.hq, w.hkv, w.dim)
+    n_wg = (w.local // bm) * (w.hq * bm // 256)
+    rec = buf.view(-1, 4).cpu().numpy()
+    assert (rec[:n_wg] != 0).all() and (rec[n_wg:] == 0).all()
+    assert (rec[:, 2] >= rec[:, 0]).all() and (rec[:, 3] >= rec[:, 1]).all()
+    busy = rec[:n_wg, 3] - rec[:n_wg, 1] > 100
+    mhz = (rec[:n_wg, 2] - rec[:n_wg, 0])[busy] / (rec[:n_wg, 3] - rec[:n_wg, 1])[busy] * 100
+    assert busy.any() and 300 < np.median(mhz) < 3000, np.median(mhz)
+
+
 def test_merge_kernel_matches_oracle():
     from context_long_attention_amd import cpattn
     rng = np.random.default_rng(3)

@@ -1,0 +1,141 @@
+"""GPU parity of the ring variants beside Pass KV (Pass Q, partial prefill, the
+gathered-KV call, the head-sharded call) against the float64 oracle, through
+the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import variants as ov
+from context_long_attention_amd import inputs
+from tests.gpu_common import assert_lse_close, assert_o_close, device_bf16, note, widen
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from context_long_attention_amd import cpattn
+    cpattn.lib()
+
+
+def _blocks(w):
+    """Seeded Q/K/V of every rank's two zigzag chunks: float64 copies and device bf16."""
+    R, c = w.cp, w.chunk
+    out = {}
+    for r in range(R):
+        a, b = oracle.zigzag_chunks(R, r)
+        q64, q = device_bf16(inputs.chunks_normal(inputs.SEED_Q, [a, b], c, w.hq, w.dim))
+        k64, k = device_bf16(inputs.chunks_normal(inputs.SEED_K, [a, b], c, w.hkv, w.dim))
+        v64, v = device_bf16(inputs.chunks_normal(inputs.SEED_V, [a, b], c, w.hkv, w.dim))
+        out[r] = dict(q64=q64, q=q, k64=k64, k=k, v64=v64, v=v, pos=oracle.zigzag_positions(w.seq_len, R, r))
+    return out
+
+
+def _pass_q_all_ranks(w, cu=None):
+    from context_long_attention_amd.variants import PassQRank
+    note(f"pass-q {w.name} S={w.seq_len} R={w.cp} Hq={w.hq} Hkv={w.hkv} D={w.dim} docs={cu is not None}")
+    B = _blocks(w)
+    gpu, ref = {}, {}
+    for r in range(w.cp):
+        rank = PassQRank(w, r, cu)
+        gpu[r] = rank.forward(B[r]["k"], B[r]["v"], lambda s: B[s]["q"])
+        ref[r] = ov.pass_q_partials(r, w.cp, lambda s: B[s]["q64"], lambda s: B[s]["pos"], B[r]["k64"], B[r]["v64"],
+                                    B[r]["pos"], cu, w.scale)
+        torch.cuda.synchronize()
+        for (s, o_t, l_t), (rs, ro, rl) in zip(gpu[r], ref[r]):
+            assert s == rs
+            assert_o_close(o_t.cpu().numpy(), ro, f"pass-q partial rank {r} owner {s}", np.isfinite(rl).T)
+            assert_lse_close(l_t.cpu().numpy(), rl, f"pass-q partial LSE rank {r} owner {s}")
+    # owners merge what every rank computed for them (host indexing for the all-to-all)
+    for owner in range(w.cp):
+        received = [(o_t, l_t) for r in range(w.cp) for s, o_t, l_t in gpu[r] if s == owner]
+        assert len(received) == w.cp
+        o, lse = PassQRank(w, owner, cu).restore(received)
+        ro, rl = ov.pass_q_restore(ref, owner)
+        torch.cuda.synchronize()
+        assert_o_close(o.cpu().numpy(), ro, f"pass-q restored O owner {owner}", np.isfinite(rl).T)
+        assert_lse_close(lse.cpu().numpy(), rl, f"pass-q restored LSE owner {owner}")
+
+
+def test_pass_q_tiny_every_rank():
+    _pass_q_all_ranks(inputs.WORKLOADS["tiny"])
+
+
+@pytest.mark.parametrize("S,R,hq,hkv,d", [(1536, 3, 6, 3, 128), (1280, 4, 16, 1, 64)])
+def test_pass_q_ragged_shapes(S, R, hq, hkv, d):
+    _pass_q_all_ranks(inputs.Workload("pq", S, R, hq, hkv, d, backward=False))
+
+
+def test_pass_q_packed_documents():
+    w = inputs.Workload("pq_docs", 2048, 4, 8, 2, 128, backward=False)
+    cu = np.array([0, 3, 300, 301, 1100, 1700, 2048], dtype=np.int32)
+    _pass_q_all_ranks(w, cu)
+
+
+@pytest.mark.parametrize("P,N,R,d", [(768, 512, 2, 128), (384, 768, 3, 64), (0, 512, 2, 128)])
+def test_partial_prefill(P, N, R, d):
+    """New tokens against the cached prefix and each other over the ring."""
+    from context_long_attention_amd.variants import PartialPrefillRank
+    hq, hkv = 8, 2
+    S = P + N
+    note(f"partial prefill P={P} N={N} R={R} D={d}")
+    q64, _ = device_bf16(inputs.chunk_normal(21, 0, S, hq, d))
+    k64, _ = device_bf16(inputs.chunk_normal(22, 0, S, hkv, d))
+    v64, _ = device_bf16(inputs.chunk_normal(23, 0, S, hkv, d))
+    dev = lambda x: torch.from_numpy(inputs.bf16_bits(x.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    for r in range(R):
+        rank = PartialPrefillRank(P, N, R, hq, hkv, d, r)
+        cached_r, new_r = ov.partial_prefill_positions(P, N, R, r)
+        parts = {s: ov.partial_prefill_positions(P, N, R, s) for s in range(R)}
+        kv = lambda s: (dev(k64[parts[s][0]]), dev(v64[parts[s][0]]), dev(k64[parts[s][1]]), dev(v64[parts[s][1]]))
+        o, lse = rank.forward(dev(q64[new_r]), kv)
+        torch.cuda.synchronize()
+        blocks = [((k64[parts[s][0]], v64[parts[s][0]], parts[s][0]), (k64[parts[s][1]], v64[parts[s][1]], parts[s][1]))
+                  for s in rank.schedule()]
+        ro, rl = ov.partial_prefill_rank(q64[new_r], new_r, blocks, d ** -0.5)
+        assert_o_close(o.cpu().numpy(), ro, f"partial prefill O rank {r}")
+        assert_lse_close(lse.cpu().numpy(), rl, f"partial prefill LSE rank {r}")
+
+
+@pytest.mark.parametrize("docs", [False, True])
+def test_gathered_call(docs):
+    from context_long_attention_amd.variants import gathered_forward
+    w = inputs.Workload("gath", 2048, 4, 8, 2, 128, backward=False)
+    note(f"gathered S={w.seq_len} docs={docs}")
+    B = _blocks(w)
+    S = w.seq_len
+    k_all64 = np.zeros((S, w.hkv, w.dim))
+    v_all64 = np.zeros((S, w.hkv, w.dim))
+    for r in range(w.cp):
+        k_all64[B[r]["pos"]] = B[r]["k64"]
+        v_all64[B[r]["pos"]] = B[r]["v64"]
+    dev = lambda x: torch.from_numpy(inputs.bf16_bits(x.astype(np.float32)).view(np.int16)).cuda().view(torch.bfloat16)
+    k_all, v_all = dev(k_all64), dev(v_all64)
+    cu = np.array([0, 1, 700, 701, 1500, S], dtype=np.int32) if docs else None
+    cu_dev = torch.from_numpy(cu).cuda() if docs else None
+    for r in (0, w.cp - 1):
+        o, lse = gathered_forward(w, r, B[r]["q"], k_all, v_all, cu_dev, 0 if cu is None else len(cu) - 1)
+        torch.cuda.synchronize()
+        ro, rl = ov.gathered_attention(B[r]["q64"], B[r]["pos"], k_all64, v_all64, w.scale, cu)
+        assert_o_close(o.cpu().numpy(), ro, f"gathered O rank {r}", np.isfinite(rl).T)
+        assert_lse_close(lse.cpu().numpy(), rl, f"gathered LSE rank {r}")
+
+
+def test_head_sharded_call():
+    from context_long_attention_amd.variants import head_sharded_forward
+    S, hq, hkv, d = 1600, 16, 4, 128
+    note(f"head-sharded S={S}")
+    q64, q = device_bf16(inputs.chunk_normal(31, 0, S, hq, d))
+    k64, k = device_bf16(inputs.chunk_normal(32, 0, S, hkv, d))
+    v64, v = device_bf16(inputs.chunk_normal(33, 0, S, hkv, d))
+    for dev_i, (qh, kvh) in enumerate([(slice(0, 4), slice(0, 1)), (slice(8, 16), slice(2, 4))]):
+        o, lse = head_sharded_forward(q[:, qh].contiguous(), k[:, kvh].contiguous(), v[:, kvh].contiguous(),
+                                      d ** -0.5)
+        torch.cuda.synchronize()
+        ro, rl = ov.head_sharded_attention(q64, k64, v64, list(range(hq))[qh], list(range(hkv))[kvh], d ** -0.5)
+        assert_o_close(o.cpu().numpy(), ro, f"head-sharded O device {dev_i}")
+        assert_lse_close(lse.cpu().numpy(), rl, f"head-sharded LSE device {dev_i}")

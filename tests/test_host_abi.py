@@ -145,6 +145,15 @@ def test_validation_rejects_bad_problems(lib):
     assert b"head_dim" in lib.cp_last_error()
 
 
+def test_clock_probe_arguments(lib):
+    """The diagnostics switch only records a pointer: it validates and returns."""
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.cp_debug_clock_probe(fake, 3) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_debug_clock_probe(None, 0) == cpattn.CP_OK
+    assert lib.cp_debug_clock_probe(fake, 4) == cpattn.CP_OK
+    assert lib.cp_debug_clock_probe(None, 0) == cpattn.CP_OK  # off again
+
+
 def test_host_cu_seqlens_checked(lib):
     D = cpattn.CP_MASK_DOC
     cu = np.array([0, 10, 5, 64], dtype=np.int32)  # not monotone
