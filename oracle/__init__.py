@@ -21,7 +21,10 @@ plain definition of softmax attention, slowly and in float64:
 * packed documents and skipping of fully masked blocks -- "Announcing
   Long-Context Training ...", section "Built on a fast attention kernel";
 * merge of partial outputs -- "Context Parallelism for Scalable Million-Token
-  Inference", section "Ring Attention Algorithms" (final output of Pass KV).
+  Inference", section "Ring Attention Algorithms" (final output of Pass KV);
+* sliding-window visibility -- "Announcing Long-Context Training ...", closing
+  section (window layers of models such as Gemma, run with a short exchange
+  between neighbouring chips).
 
 Pins: every function is checked by ``tests/test_oracle_*.py`` against the
 pages' worked example, closed forms, library routines and brute force.  The

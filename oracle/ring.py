@@ -63,30 +63,38 @@ def document_index(positions: np.ndarray, cu_seqlens: np.ndarray) -> np.ndarray:
     return np.searchsorted(cu, np.asarray(positions, dtype=np.int64), side="right") - 1
 
 
-def visibility(qpos: np.ndarray, kpos: np.ndarray, cu_seqlens=None) -> np.ndarray:
+def visibility(qpos: np.ndarray, kpos: np.ndarray, cu_seqlens=None, window=None) -> np.ndarray:
     """Boolean [n, m]: may the query at qpos[i] attend to the key at kpos[j]?
 
     Causal prefill: a token sees itself and every earlier token ("Context
     Parallelism for Scalable Million-Token Inference", section "Attention
     Compute Patterns in Multi-Turn Chat").  With packed documents a token
     additionally sees only tokens of its own document ("Announcing Long-Context
-    Training ...", section "Built on a fast attention kernel").
+    Training ...", section "Built on a fast attention kernel").  A sliding
+    window of ``window`` tokens ("Announcing Long-Context Training ...", the
+    closing section on window layers of models such as Gemma) further limits a
+    token to the ``window`` most recent positions, itself included: key k is
+    visible to query q iff q - window < k <= q.  ``window`` None or 0 means
+    no window.
     """
     qpos = np.asarray(qpos, dtype=np.int64)
     kpos = np.asarray(kpos, dtype=np.int64)
     vis = kpos[None, :] <= qpos[:, None]
+    if window:
+        vis &= (qpos[:, None] - kpos[None, :]) < int(window)
     if cu_seqlens is not None:
         vis &= document_index(kpos, cu_seqlens)[None, :] == document_index(qpos, cu_seqlens)[:, None]
     return vis
 
 
-def chunk_pair_class(qpos_chunk: np.ndarray, kpos_chunk: np.ndarray, cu_seqlens=None) -> int:
+def chunk_pair_class(qpos_chunk: np.ndarray, kpos_chunk: np.ndarray, cu_seqlens=None, window=None) -> int:
     """Brute-force class of one (query chunk, key chunk) pair from its visibility block.
 
     No visible pair: SKIP.  With packed documents every other pair is DOC.
-    Otherwise: every pair visible and the chunks distinct: FULL; else DIAG.
+    Otherwise: every pair visible and the chunks distinct: FULL; else DIAG
+    (the causal diagonal, or a pair that the sliding window cuts).
     """
-    vis = visibility(qpos_chunk, kpos_chunk, cu_seqlens)
+    vis = visibility(qpos_chunk, kpos_chunk, cu_seqlens, window)
     if not vis.any():
         return CLS_SKIP
     if cu_seqlens is not None:
@@ -106,7 +114,7 @@ def _tiles(segments, size):
     return out
 
 
-def tile_map(q_segments, kv_segments, bm: int, bn: int, cu_seqlens=None) -> np.ndarray:
+def tile_map(q_segments, kv_segments, bm: int, bn: int, cu_seqlens=None, window=None) -> np.ndarray:
     """Block map of one step by brute force: uint8 [query tiles, key tiles].
 
     Segments are (global start position, length); tiles of ``bm`` query rows and
@@ -123,7 +131,7 @@ def tile_map(q_segments, kv_segments, bm: int, bn: int, cu_seqlens=None) -> np.n
     for i, (q0, ql) in enumerate(qt):
         qpos = np.arange(q0, q0 + ql)
         for j, (k0, kl) in enumerate(kt):
-            vis = visibility(qpos, np.arange(k0, k0 + kl), cu_seqlens)
+            vis = visibility(qpos, np.arange(k0, k0 + kl), cu_seqlens, window)
             if vis.all():
                 out[i, j] = TILE_FULL
             elif vis.any():
@@ -249,12 +257,13 @@ def attention_backward_partial(q, k, v, do, lse, delta, vis, scale):
 # --------------------------------------------------------------------------------------
 # One rank's whole ring
 # --------------------------------------------------------------------------------------
-def rank_forward(q_local, qpos, kv_blocks, cu_seqlens, scale, rows=None):
+def rank_forward(q_local, qpos, kv_blocks, cu_seqlens, scale, rows=None, window=None):
     """Replay one rank's R forward steps and merge them step by step.
 
     ``kv_blocks`` lists, in ring order, (k, v, kpos) of the block held at each
     step.  ``rows`` optionally restricts the computation to a subset of local
-    query rows (the result then covers only those rows).
+    query rows (the result then covers only those rows).  ``window`` is the
+    sliding window of ``visibility``.
     Returns (O, LSE, per-step list of (O_t, LSE_t)).
     """
     if rows is not None:
@@ -265,14 +274,14 @@ def rank_forward(q_local, qpos, kv_blocks, cu_seqlens, scale, rows=None):
     lse = np.full((hq, n), -np.inf)
     steps = []
     for k, v, kpos in kv_blocks:
-        vis = visibility(qpos, kpos, cu_seqlens)
+        vis = visibility(qpos, kpos, cu_seqlens, window)
         o_t, lse_t = attention_partial(q_local, k, v, vis, scale)
         steps.append((o_t, lse_t))
         o, lse = merge(o, lse, o_t, lse_t)
     return o, lse, steps
 
 
-def rank_backward(q_local, qpos, do_local, o, lse, kv_blocks, cu_seqlens, scale):
+def rank_backward(q_local, qpos, do_local, o, lse, kv_blocks, cu_seqlens, scale, window=None):
     """Replay one rank's R backward steps from the final O and LSE.
 
     dQ accumulates over the steps; dK/dV are returned per step (the part of the
@@ -282,15 +291,15 @@ def rank_backward(q_local, qpos, do_local, o, lse, kv_blocks, cu_seqlens, scale)
     dq = np.zeros(np.asarray(q_local).shape)
     per_step = []
     for k, v, kpos in kv_blocks:
-        vis = visibility(qpos, kpos, cu_seqlens)
+        vis = visibility(qpos, kpos, cu_seqlens, window)
         dq_t, dk_t, dv_t = attention_backward_partial(q_local, k, v, do_local, lse, delta, vis, scale)
         dq += dq_t
         per_step.append((dk_t, dv_t))
     return dq, per_step, delta
 
 
-def causal_flops(qpos, kpos, hq, dim, cu_seqlens=None, backward=False):
+def causal_flops(qpos, kpos, hq, dim, cu_seqlens=None, backward=False, window=None):
     """Causal-counted FLOPs of one step: 4*D (forward) or 10*D (backward) per
     visible (query, key) pair and query head.  Convention only: parity unpinned."""
-    pairs = int(visibility(qpos, kpos, cu_seqlens).sum())
+    pairs = int(visibility(qpos, kpos, cu_seqlens, window).sum())
     return pairs * hq * dim * (10 if backward else 4)
