@@ -18,11 +18,15 @@
 //  * K/V tiles move HBM -> LDS with direct buffer loads (rows past a ragged
 //    tile read as zero) into a ring of four K and four V buffers, three tiles
 //    ahead of use; each step waits only for the tiles the next step reads.
-//  * Rotated pipeline: the P V product of tile i-1 overlaps the mask and row
-//    max of tile i; the scores of tile i+1 overlap the exponentials of tile i.
-//  * The reference maximum is raised only when a row's maximum grows by more
-//    than 2^8 in the exp2 domain, so the accumulator is rescaled rarely; P is
-//    then bounded by 256, which fp32 accumulation and bf16 rounding absorb.
+//  * Rotated pipeline: one step alternates the MFMAs of the P V product of
+//    tile i-1 and of the scores of tile i+1, with the exponentials, row sum and
+//    bf16 convert of tile i spread over them.
+//  * No running row maximum on the fast path: exponentials are taken against a
+//    reference set by a row's first visible tile.  A row whose tile sum
+//    exceeds 2^20 or is not finite (or that has no reference yet) takes a slow
+//    path that raises the reference to the tile's true maximum, rescales and
+//    recomputes the tile.  P then stays below 2^20, which fp32 accumulation
+//    and bf16 rounding hold without loss of relative precision.
 //  * Tiles with no visible pair are never visited (block-sparse skip); the
 //    element mask runs only on partially visible or ragged tiles.
 //  * Work items are dealt to the XCDs round-robin: each XCD keeps the same head
@@ -262,7 +266,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     // flight; everything older (the tiles the next step reads) has landed.
     constexpr int kPending = 2 * 2 * (L::NBLK / kWaves);
 
-    bf16x8 pb[4];  // P of the previous tile (bf16), consumed by the next step's P V
+    bf16x8 pa[4], pbb[4];  // P (bf16) of two consecutive tiles: one being made, one consumed by P V
 
     // Element mask of tile it's scores on partial or ragged tiles: key k of the
     // tile is visible iff lo_lim <= k <= hi_lim, tested as one unsigned range
@@ -299,37 +303,92 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         return __builtin_bit_cast(bf16x8, a);
     };
     constexpr int kPV = 4 * DB;  // MFMAs of one P V product
-
-    // Raise the reference maximum when the tile's row maximum exceeds it by more
-    // than 2^8 (in the exp2 domain), rescaling the running sum and accumulator.
-    auto update_max = [&](float mloc) {
-        const float mt2 = mloc * c2;
-        const bool raise = mt2 > m2 + 8.f;
-        if (__any(raise)) {
-            const float m2n = raise ? mt2 : m2;
-            const float alpha = (m2n == m2) ? 1.f : __builtin_amdgcn_exp2f(m2 - m2n);
-            l_run *= alpha;
-#pragma unroll
-            for (int db = 0; db < DB; ++db) acc[db] *= alpha;
-            m2 = m2n;
-        }
+    constexpr int kS = 2 * DS;   // MFMAs of one tile's scores
+    static_assert(kPV == kS, "the step alternates P V and score MFMAs");
+    constexpr int kEPM = 32 / (kPV + kS);  // scores of this lane per MFMA of a step (1 at D = 128, 2 at D = 64)
+    // MFMA i of a tile's scores: head-dim step i / 2, key block i % 2
+    auto k_operand = [&](lds_char* kbase, int i) -> bf16x8 {
+        return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
+            kbase + L::off(32 * (i & 1), 16 * (i >> 1)));
     };
 
-    // Scores of the next tile (2 DS MFMAs, K from LDS read two ahead) with the
-    // exponentials, bf16 P and row sum of tile it spread over them: MFMA i is
-    // followed by elements 2i and 2i+1 of this lane's 32 scores (fma, exp, sum,
-    // one packed bf16 convert).  sched_barrier keeps each slice in this order.
-    auto scores_and_exp = [&](const char* k_read, const f32x16* cur, f32x16* nxt) {
+    // Exponential of this lane's scores e, e + 1 against the reference maximum:
+    // P = 2^(c2 s - m2) as two fp32 values (for the row sum) and one packed bf16 pair.
+    auto exp_pair = [&](const f32x16* cur, int e, float nb, float& x0, float& x1) -> uint32_t {
+        x0 = __builtin_amdgcn_exp2f(fmaf(cur[e >> 4][e & 15], c2, nb));
+        x1 = __builtin_amdgcn_exp2f(fmaf(cur[e >> 4][(e & 15) + 1], c2, nb));
+        const f32x2 two = {x0, x1};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
+    };
+    auto pack_p = [&](const uint32_t* pbits, bf16x8* pout) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+            const u32x4 w = {pbits[4 * q4], pbits[4 * q4 + 1], pbits[4 * q4 + 2], pbits[4 * q4 + 3]};
+            pout[q4] = __builtin_bit_cast(bf16x8, w);
+            materialise(pout[q4]);
+        }
+    };
+    // The row maximum of a tile's scores (both half-waves), in the exp2 domain.
+    auto tile_max2 = [&](const f32x16* cur) -> float {
+        float mloc = cur[0][0];
+#pragma unroll
+        for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, cur[0][r]);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, cur[1][r]);
+        return max_halves(mloc) * c2;
+    };
+    // Move the reference maximum up to mt2 where it is larger, rescaling the row
+    // sum and the accumulator (from -inf: both are still zero).
+    auto raise_max = [&](float mt2) {
+        const float m2n = fmaxf(m2, mt2);
+        const float alpha = (m2n == m2) ? 1.f : __builtin_amdgcn_exp2f(m2 - m2n);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        m2 = m2n;
+    };
+    // P of a whole tile (no interleaving): its row sum, bf16 P into pout.
+    auto tile_exp = [&](const f32x16* cur, bf16x8* pout) -> float {
+        const float nb = (m2 == -INFINITY) ? 0.f : -m2;
+        float sa = 0.f, sb = 0.f;
+        uint32_t pbits[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float x0, x1;
+            pbits[i] = exp_pair(cur, 2 * i, nb, x0, x1);
+            sa += x0;
+            sb += x1;
+        }
+        pack_p(pbits, pout);
+        return sa + sb;
+    };
+
+    // The reference maximum m2 is not tracked tile by tile.  Exponentials are
+    // taken against the current m2 and a row whose tile sum exceeds kPMax (or is
+    // not finite), or that has no reference yet, takes the slow path: the tile's
+    // true maximum raises m2, the accumulator and row sum are rescaled and the
+    // tile's P is recomputed.  P then never exceeds kPMax, which bf16 and fp32
+    // hold exactly in range; the P of a tile is only consumed by the next step's
+    // P V, after this check.
+    constexpr float kPMax = 1048576.f;  // 2^20
+    auto check_tile = [&](const f32x16* cur, bf16x8* pout, float tsum) -> float {
+        const bool bad = (m2 == -INFINITY) || !(tsum <= kPMax);
+        if (__any(bad)) {
+            raise_max(tile_max2(cur));
+            tsum = tile_exp(cur, pout);
+        }
+        return tsum;
+    };
+
+    // Scores of tile 1 (16 MFMAs, K read two ahead) with the exponentials, bf16
+    // P and row sum of tile 0 spread over them (prologue; tile 0's maximum is
+    // already the reference).
+    auto scores_and_exp = [&](const char* k_read, const f32x16* cur, f32x16* nxt, bf16x8* pout) -> float {
         lds_char* kbase = lds_base(k_read, k_lane);
         const float nb = (m2 == -INFINITY) ? 0.f : -m2;
-        auto k_operand = [&](int i) -> bf16x8 {  // MFMA i: head-dim step i / 2, key block i % 2
-            return *reinterpret_cast<const __attribute__((address_space(3))) bf16x8*>(
-                kbase + L::off(32 * (i & 1), 16 * (i >> 1)));
-        };
-        constexpr int kS = 2 * DS;
         bf16x8 ka[3];
-        ka[0] = k_operand(0);
-        ka[1] = k_operand(1);
+        ka[0] = k_operand(kbase, 0);
+        ka[1] = k_operand(kbase, 1);
         nxt[0] = f32x16{};
         nxt[1] = f32x16{};
         float sa = 0.f, sb = 0.f;
@@ -337,75 +396,96 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             if (i + 2 < kS) {
-                ka[(i + 2) % 3] = k_operand(i + 2);
+                ka[(i + 2) % 3] = k_operand(kbase, i + 2);
                 order_memory();
             }
             if (i < kS) {
                 nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf[i >> 1], nxt[i & 1], 0, 0, 0);
                 pin(nxt[i & 1]);
             }
-            const int e = 2 * i;  // elements e, e + 1: register (e % 16) of block e / 16
-            const float x0 = __builtin_amdgcn_exp2f(fmaf(cur[e >> 4][e & 15], c2, nb));
-            const float x1 = __builtin_amdgcn_exp2f(fmaf(cur[e >> 4][(e & 15) + 1], c2, nb));
+            float x0, x1;
+            pbits[i] = exp_pair(cur, 2 * i, nb, x0, x1);
             sa += x0;
             sb += x1;
-            const f32x2 two = {x0, x1};
-            pbits[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
             pin(pbits[i]);
             pin(sa);
             pin(sb);
         }
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-            const u32x4 w = {pbits[4 * q4], pbits[4 * q4 + 1], pbits[4 * q4 + 2], pbits[4 * q4 + 3]};
-            pb[q4] = __builtin_bit_cast(bf16x8, w);
-            materialise(pb[q4]);
-        }
-        l_run += sa + sb;
-        materialise(l_run);
+        pack_p(pbits, pout);
+        return sa + sb;
     };
 
-    // Rotated pipeline step it (1 <= it < n_it):
-    //   loads:  K(it+4) into the K slot freed by K(it), V(it+2) into the V slot freed by V(it-2);
+    // Pipeline step it (1 <= it < n_it):
     //   mask of tile it (partial tiles only);
-    //   O^T += V(it-1)^T P(it-1) (MFMA) interleaved with tile it's row maximum (VALU);
-    //   rare rescale;
-    //   scores of tile it+1 (MFMA) interleaved with exp / sum / bf16 of tile it (VALU) -> P(it).
+    //   loads (issued after the fourth MFMA): K(it+4) into the K slot freed by
+    //   K(it), V(it+2) into the V slot freed by V(it-2);
+    //   32 MFMAs alternating O^T += V(it-1)^T P(it-1) and the scores of tile it+1,
+    //   with the exponential, bf16 convert and row sum of one score of tile it
+    //   after each (P(it) into p_new);
+    //   the slow-path check of tile it.
     // Slots: K(j) and V(j) live in slot j mod 4, so each unrolled copy below
     // touches statically known buffers.
-    auto step = [&](int it, f32x16* cur, f32x16* nxt, char* k_fill, const char* k_read, char* v_fill,
-                    const char* v_read) {
-        issue(false, it + 4, k_fill);
-        issue(true, it + 2, v_fill);
+    auto step = [&](int it, f32x16* cur, f32x16* nxt, const bf16x8* p_old, bf16x8* p_new, char* k_fill,
+                    const char* k_read, char* v_fill, const char* v_read) {
         mask_tile(it, cur);
-        // P V of the previous tile (V read two MFMAs ahead) with two row-maximum
-        // steps of this tile after each MFMA
         lds_char* vbase = lds_base(v_read, v_lane);
-        bf16x8 va[3];
+        lds_char* kbase = lds_base(k_read, k_lane);
+        const float nb = (m2 == -INFINITY) ? 0.f : -m2;
+        bf16x8 va[3], ka[3];
         va[0] = v_operand(vbase, 0);
+        ka[0] = k_operand(kbase, 0);
         va[1] = v_operand(vbase, 1);
-        float ma = cur[0][0], mb = cur[1][0];
+        ka[1] = k_operand(kbase, 1);
+        nxt[0] = f32x16{};
+        nxt[1] = f32x16{};
+        float sa = 0.f, sb = 0.f, x_prev = 0.f;
+        uint32_t pbits[16];
 #pragma unroll
-        for (int i = 0; i < kPV; ++i) {
-            if (i + 2 < kPV) {
-                va[(i + 2) % 3] = v_operand(vbase, i + 2);
+        for (int j = 0; j < kPV + kS; ++j) {
+            const int i = j >> 1;
+            if ((j & 1) == 0) {
+                if (i + 2 < kPV) {
+                    va[(i + 2) % 3] = v_operand(vbase, i + 2);
+                    order_memory();
+                }
+                acc[i % DB] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], p_old[i / DB], acc[i % DB], 0, 0, 0);
+                pin(acc[i % DB]);
+            } else {
+                if (i + 2 < kS) {
+                    ka[(i + 2) % 3] = k_operand(kbase, i + 2);
+                    order_memory();
+                }
+                nxt[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf[i >> 1], nxt[i & 1], 0, 0, 0);
+                pin(nxt[i & 1]);
+            }
+            if (j == 3) {
+                // this step's loads, issued a few MFMAs in so that their address
+                // arithmetic is off the path from the barrier to the first MFMA
+                issue(false, it + 4, k_fill);
+                issue(true, it + 2, v_fill);
                 order_memory();
             }
-            acc[i % DB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[i / DB], acc[i % DB], 0, 0, 0);
-            pin(acc[i % DB]);
+            // scores e of this lane (register e % 16 of block e / 16)
 #pragma unroll
-            for (int r = (32 * i) / kPV; r < (32 * (i + 1)) / kPV; ++r)
-                if (r % 16) {
-                    if (r < 16)
-                        ma = fmaxf(ma, cur[0][r]);
-                    else
-                        mb = fmaxf(mb, cur[1][r - 16]);
+            for (int u = 0; u < kEPM; ++u) {
+                const int e = j * kEPM + u;
+                const float x = __builtin_amdgcn_exp2f(fmaf(cur[e >> 4][e & 15], c2, nb));
+                if ((e & 1) == 0) {
+                    sa += x;
+                    x_prev = x;
+                    pin(sa);
+                } else {
+                    sb += x;
+                    const f32x2 two = {x_prev, x};
+                    pbits[e >> 1] = __builtin_bit_cast(uint32_t, __builtin_convertvector(two, bf16x2));
+                    pin(pbits[e >> 1]);
+                    pin(sb);
                 }
-            pin(ma);
-            pin(mb);
+            }
         }
-        update_max(max_halves(fmaxf(ma, mb)));
-        scores_and_exp(k_read, cur, nxt);
+        pack_p(pbits, p_new);
+        l_run += check_tile(cur, p_new, sa + sb);
         ring_barrier<kPending>();  // the tiles the next step reads have landed; this step's slots are free
     };
 
@@ -421,33 +501,33 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         issue(true, 1, vb1);
         issue(false, 3, kb3);
         ring_barrier<kPending>();  // every wave has read K(0), so its slot can be refilled
-        // step 0: no P V yet
+        // step 0: no P V yet; tile 0's maximum sets the reference
         issue(false, 4, kb0);
         issue(true, 2, vb2);
         mask_tile(0, sa);
-        {
-            float mloc = sa[0][0];
-#pragma unroll
-            for (int r = 1; r < 16; ++r) mloc = fmaxf(mloc, sa[0][r]);
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mloc = fmaxf(mloc, sa[1][r]);
-            update_max(max_halves(mloc));
-        }
-        scores_and_exp(kb1, sa, sb);
+        raise_max(tile_max2(sa));
+        l_run += scores_and_exp(kb1, sa, sb, pa);
         ring_barrier<kPending>();
         for (int it = 1; it < n_it; it += 4) {
-            step(it, sb, sa, kb1, kb2, vb3, vb0);
-            if (it + 1 < n_it) step(it + 1, sa, sb, kb2, kb3, vb0, vb1);
-            if (it + 2 < n_it) step(it + 2, sb, sa, kb3, kb0, vb1, vb2);
-            if (it + 3 < n_it) step(it + 3, sa, sb, kb0, kb1, vb2, vb3);
+            step(it, sb, sa, pa, pbb, kb1, kb2, vb3, vb0);
+            if (it + 1 < n_it) step(it + 1, sa, sb, pbb, pa, kb2, kb3, vb0, vb1);
+            if (it + 2 < n_it) step(it + 2, sb, sa, pa, pbb, kb3, kb0, vb1, vb2);
+            if (it + 3 < n_it) step(it + 3, sa, sb, pbb, pa, kb0, kb1, vb2, vb3);
         }
-        // the last P V: V(n_it - 1) landed at the last step's barrier
+        // the last P V: V(n_it - 1) landed at the last step's barrier; P(j)
+        // lives in pa for even j and in pbb for odd j
         const int last = (n_it - 1) & 3;
         lds_char* v_last = lds_base((last == 0) ? vb0 : (last == 1) ? vb1 : (last == 2) ? vb2 : vb3, v_lane);
+        auto last_pv = [&](const bf16x8* pl) {
 #pragma unroll
-        for (int i = 0; i < kPV; ++i)
-            acc[i % DB] =
-                __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(v_last, i), pb[i / DB], acc[i % DB], 0, 0, 0);
+            for (int i = 0; i < kPV; ++i)
+                acc[i % DB] =
+                    __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand(v_last, i), pl[i / DB], acc[i % DB], 0, 0, 0);
+        };
+        if (last & 1)
+            last_pv(pbb);
+        else
+            last_pv(pa);
     }
 
     // ---- epilogue: normalise and write O (fp32) and LSE (natural log), or
