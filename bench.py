@@ -346,6 +346,51 @@ def measure_variants(torch, w, rank, steps, warmup):
     return out
 
 
+def measure_window(torch, w, rank, steps, warmup):
+    """A sliding-window layer (the pages' window layers of models such as Gemma):
+    forward and backward ring of one rank, where only the blocks with visible
+    pairs (the rank's own and its neighbours') are received and computed."""
+    from context_long_attention_amd import cpattn, inputs
+    from context_long_attention_amd.ring import RankRing
+    q, kv = make_rank_inputs(torch, w, rank)
+    c = w.chunk
+    pos = cpattn.cp_partition_zigzag(w.seq_len, w.cp, rank)
+    d_o = _dev_bf16(torch, inputs.chunks_normal(inputs.SEED_DO, [int(pos[0]) // c, int(pos[c]) // c], c, w.hq,
+                                                w.dim))
+    ring = RankRing(w, rank)
+    pairs = sum(ring.step_pairs(t) for t in range(w.cp))
+    live = [t for t in range(w.cp) if t == 0 or ring.source_live(ring.schedule()[t])]
+    fwd_timer, bwd_timer = KernelTimer(torch, "fwd"), KernelTimer(torch, "bwd")
+
+    def timer(step, what, stream):
+        fwd_timer(step, what, stream)
+        bwd_timer(step, what, stream)
+
+    def one_step(tm):
+        r = RankRing(w, rank)
+        o, lse, _ = r.forward(q, kv.__getitem__, stage=True, timer=tm)
+        r.backward(q, d_o, o, lse, kv.__getitem__, stage=True, keep_steps=False, timer=tm)
+
+    for _ in range(warmup):
+        one_step(None)
+    torch.cuda.synchronize()
+    fwd_timer.enabled = bwd_timer.enabled = True
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        one_step(timer)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    f_fwd, f_bwd = pairs * w.hq * w.dim * 4, pairs * w.hq * w.dim * 10
+    log(f"{w.name}: {ms:.3f} ms/step, live steps {live}")
+    return {"workload": f"{w.name}: window {w.window} over S={w.seq_len} at CP={w.cp}, rank {rank}, fwd+bwd",
+            "window": w.window, "live_steps": live, "pairs_per_head": pairs,
+            "tflops": round(tflops(f_fwd + f_bwd, ms), 2), "ms_per_step": round(ms, 4),
+            "fwd_kernel_tflops": round(tflops(f_fwd, fwd_timer.total_ms() / steps), 2),
+            "bwd_kernel_tflops": round(tflops(f_bwd, bwd_timer.total_ms() / steps), 2)}
+
+
 def tflops(flops, ms):
     return flops / (ms * 1e-3) / 1e12
 
@@ -362,6 +407,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the Pass Q / prefill / gathered legs")
+    ap.add_argument("--no-window", action="store_true", help="skip the sliding-window layer leg")
+    ap.add_argument("--window-workload", default="llama3_8b_window4k")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first make 3 device-to-device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -434,6 +481,9 @@ def main():
         }
     if not args.no_variants:
         record["variants"] = measure_variants(torch, w, args.rank, max(1, args.steps // 2), 1)
+    if not args.no_window:
+        record["sliding_window"] = measure_window(torch, inputs.WORKLOADS[args.window_workload], args.rank,
+                                                  max(1, args.steps // 2), 1)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host (cpu_baseline)")
         record["cpu_baseline"] = cpu_baseline(w, args.rank, args.cpu_heads)

@@ -23,7 +23,7 @@ CP_TILE_SKIP, CP_TILE_PARTIAL, CP_TILE_FULL = 0, 1, 2
 # Every symbol include/cpattn.h declares.
 EXPORTS = (
     "cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition_zigzag", "cp_ring_source",
-    "cp_step_masks", "cp_tile_shape", "cp_block_map_size", "cp_block_map", "cp_count_pairs",
+    "cp_step_masks", "cp_step_masks_window", "cp_tile_shape", "cp_block_map_size", "cp_block_map", "cp_count_pairs",
     "cp_attn_fwd_step", "cp_merge_partials", "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step",
     "cp_debug_clock_probe",
 )
@@ -48,6 +48,7 @@ class cp_attn_problem(ctypes.Structure):
         ("q_seg", cp_segment * 2), ("kv_seg", cp_segment * 2),
         ("mask", (ctypes.c_int32 * 2) * 2),
         ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
+        ("window", ctypes.c_int32),
     ]
 
 
@@ -71,6 +72,7 @@ def lib():
             "cp_partition_zigzag": ([i64, i32, i32, vp], i32),
             "cp_ring_source": ([i32, i32, i32, vp], i32),
             "cp_step_masks": ([i32, i32, i32, i32, vp], i32),
+            "cp_step_masks_window": ([i64, i32, i32, i32, i32, i64, vp], i32),
             "cp_tile_shape": ([i32, i32, i32, vp, vp], i32),
             "cp_block_map_size": ([P, vp, vp], i32),
             "cp_block_map": ([P, vp], i32),
@@ -136,6 +138,13 @@ def cp_step_masks(cp_size: int, rank: int, step: int, packed: bool) -> list[list
     return [[out[0], out[1]], [out[2], out[3]]]
 
 
+def cp_step_masks_window(seq_len: int, cp_size: int, rank: int, step: int, packed: bool,
+                         window: int) -> list[list[int]]:
+    out = (ctypes.c_int32 * 4)()
+    _check(lib().cp_step_masks_window(seq_len, cp_size, rank, step, int(bool(packed)), window, out))
+    return [[out[0], out[1]], [out[2], out[3]]]
+
+
 def cp_tile_shape(hq: int, hkv: int, head_dim: int) -> tuple[int, int]:
     bm, bn = ctypes.c_int32(), ctypes.c_int32()
     _check(lib().cp_tile_shape(hq, hkv, head_dim, ctypes.byref(bm), ctypes.byref(bn)))
@@ -143,8 +152,9 @@ def cp_tile_shape(hq: int, hkv: int, head_dim: int) -> tuple[int, int]:
 
 
 def make_problem(hq, hkv, head_dim, scale, q_rows, kv_rows, q_segments, kv_segments, masks,
-                 cu_seqlens_ptr=None, n_docs=0) -> cp_attn_problem:
-    """Fill a cp_attn_problem.  Segments are (row0, pos0, len) triples."""
+                 cu_seqlens_ptr=None, n_docs=0, window=0) -> cp_attn_problem:
+    """Fill a cp_attn_problem.  Segments are (row0, pos0, len) triples; window is
+    the sliding window in tokens (0: none)."""
     p = cp_attn_problem()
     p.hq, p.hkv, p.head_dim, p.scale = hq, hkv, head_dim, scale
     p.q_rows, p.kv_rows = q_rows, kv_rows
@@ -158,6 +168,7 @@ def make_problem(hq, hkv, head_dim, scale, q_rows, kv_rows, q_segments, kv_segme
             p.mask[i][j] = masks[i][j] if (i < len(q_segments) and j < len(kv_segments)) else CP_MASK_SKIP
     p.cu_seqlens = cu_seqlens_ptr
     p.n_docs = n_docs
+    p.window = window
     return p
 
 

@@ -51,6 +51,7 @@ struct BwdParams {
     float* dv;
     const int32_t* cu;
     int32_t n_docs;
+    int32_t window;  // sliding window (0: none)
     int32_t hq, hkv, group;
     int32_t q_rows;
     float scale, scale_log2;
@@ -132,7 +133,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
         }
     }
 
-    // ---- document ends: (query q, key k) is visible iff k <= q < end of k's document
+    // ---- query ends: (query q, key k) is visible iff k <= q < qend(k), with qend
+    // the end of k's document (DOC) and k + window (sliding window, DIAG and
+    // DOC), whichever is earlier; non-decreasing in k
     bool any_doc = false;
     for (int qs = 0; qs < p.nq_seg; ++qs) any_doc |= (p.mask[qs][s] == CP_MASK_DOC);
     int kend_lane = 0x7fffffff, kend_first = 0x7fffffff, kend_last = 0x7fffffff;
@@ -145,6 +148,12 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
         }
         kend_lane = p.cu[j + 1];
     }
+    const int win = p.window;
+    auto win_end = [&](int k) { return (win > 0 && k <= 0x7fffffff - win) ? k + win : 0x7fffffff; };
+    const int wend_lane = win_end(kp), wend_first = win_end(k0p), wend_last = win_end(k1p);
+    auto qend = [](int m, int doc_end, int w_end) {
+        return (m == CP_MASK_DOC) ? min(doc_end, w_end) : (m == CP_MASK_DIAG_CAUSAL ? w_end : 0x7fffffff);
+    };
 
     // ---- query tiles (per query segment) that see any key of [k0p, k1p]
     int tlo[2] = {0, 0}, thi[2] = {0, 0};
@@ -162,8 +171,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
         if (k0p > ppos + plen - 1) continue;  // causal: rows q >= k0p
         const int lo = (k0p <= ppos) ? 0 : (k0p - ppos) / BQ;
         int hi = nqt;
-        if (m == CP_MASK_DOC) {  // and q < end of the last key's document
-            const int qmax = kend_last - 1;
+        const int qe = qend(m, kend_last, wend_last);  // and q < qend of the last key
+        if (qe != 0x7fffffff) {
+            const int qmax = qe - 1;
             hi = (qmax < ppos) ? 0 : min(nqt, (qmax - ppos) / BQ + 1);
         }
         if (lo < hi) {
@@ -234,9 +244,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
 
         // P = exp2(c2 s - log2e LSE) and dS = P (dP - delta); rows past a ragged tile
         // have zero Q and dO and contribute nothing, so only visibility is masked
-        const bool full = (m == CP_MASK_FULL) || (k1p <= qpos0 && qpos0 + qrows - 1 < kend_first);
+        const bool full = (m == CP_MASK_FULL) || (k1p <= qpos0 && qpos0 + qrows - 1 < qend(m, kend_first, wend_first));
         const int qk = qpos0 - kp + 4 * hl;                              // q - k without the register's offset
-        const unsigned span = (unsigned)((m == CP_MASK_DOC ? kend_lane : 0x7fffffff) - kp);
+        const unsigned span = (unsigned)(qend(m, kend_lane, wend_lane) - kp);
         const float* lse_row = reinterpret_cast<const float*>(asl);
         const float* del_row = reinterpret_cast<const float*>(asl + 256);
         f32x16 pr, dsr;
@@ -379,8 +389,16 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
     const int mk1 = (p.nkv_seg > 1) ? p.mask[qs][1] : CP_MASK_SKIP;
     const int len0 = p.ks_len[0], len1 = p.ks_len[1];
     const int pos0 = p.ks_pos0[0], pos1 = p.ks_pos0[1];
-    const SegRange r0 = key_tile_range<kBN>(mk0, q0, q1, mk0 == CP_MASK_DOC ? lo0 : 0, pos0, len0);
-    const SegRange r1 = (p.nkv_seg > 1) ? key_tile_range<kBN>(mk1, q0, q1, mk1 == CP_MASK_DOC ? lo0 : 0, pos1, len1)
+    // first visible key of a row (document start, window start), as in the forward kernel
+    const int win = p.window;
+    const int wlo0 = (win > 0) ? q0 - win + 1 : 0, wlo1 = (win > 0) ? q1 - win + 1 : 0;
+    const int my_wlo = (win > 0) ? my_pos - win + 1 : 0;
+    auto lower = [](int m, int doc_lo, int win_lo) {
+        return (m == CP_MASK_DOC) ? max(doc_lo, win_lo) : (m == CP_MASK_DIAG_CAUSAL ? win_lo : 0);
+    };
+    const int my_lo_doc = max(my_lo, my_wlo);
+    const SegRange r0 = key_tile_range<kBN>(mk0, q0, q1, lower(mk0, lo0, wlo0), pos0, len0);
+    const SegRange r1 = (p.nkv_seg > 1) ? key_tile_range<kBN>(mk1, q0, q1, lower(mk1, lo0, wlo0), pos1, len1)
                                         : SegRange{0, 0};
     const int tlo0 = r0.t_lo, tlo1 = r1.t_lo;
     const int n0 = r0.t_hi - r0.t_lo;
@@ -469,7 +487,7 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
         const int kcount = min(kBN, tr.len - tr.t * kBN);
         const int kp0 = tr.pos + tr.t * kBN;
         const int m = tr.mask;
-        const bool full = key_tile_full<kBN>(m, q0, m == CP_MASK_DOC ? lo1 : 0, tr.pos, tr.len, tr.t);
+        const bool full = key_tile_full<kBN>(m, q0, lower(m, lo1, wlo1), tr.pos, tr.len, tr.t);
         bool vis_all = true;
         int lo_l = 0;
         unsigned span = 0;
@@ -480,7 +498,7 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
             int lo_lim = 0;
             if (m != CP_MASK_FULL) {
                 hi_lim = min(hi_lim, my_pos - kp0);
-                if (m == CP_MASK_DOC) lo_lim = max(0, my_lo - kp0);
+                lo_lim = max(0, ((m == CP_MASK_DOC) ? my_lo_doc : my_wlo) - kp0);
             }
             lo_l = lo_lim - 4 * hl;
             span = (unsigned)(hi_lim - lo_lim);
@@ -585,6 +603,7 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     prm.dv = dv_out;
     prm.cu = p->cu_seqlens;
     prm.n_docs = p->n_docs;
+    prm.window = p->window;
     prm.hq = p->hq;
     prm.hkv = p->hkv;
     prm.group = p->hq / p->hkv;

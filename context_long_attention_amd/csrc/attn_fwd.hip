@@ -64,6 +64,7 @@ struct FwdParams {
     const int32_t* cu;
     uint8_t* tile_map;
     int32_t n_docs;
+    int32_t window;  // sliding window (0: none)
     int32_t hq, hkv, group;
     int32_t q_rows;
     float scale, scale_log2;
@@ -162,12 +163,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         }
         my_lo = p.cu[j];
     }
-    const SegRange r0 = key_tile_range<kBN>(mk0, q0, q1, mk0 == CP_MASK_DOC ? lo0 : 0, pos0, len0);
-    const SegRange r1 = key_tile_range<kBN>(mk1, q0, q1, mk1 == CP_MASK_DOC ? lo0 : 0, pos1, len1);
+    // First visible key of a row under a pair's mask: the document start (DOC)
+    // and, with a sliding window, position - window + 1 (DIAG and DOC); 0 is no
+    // bound (positions are >= 0).  Non-decreasing in the row and <= the row.
+    const int win = sreg(p.window);
+    const int wlo0 = (win > 0) ? q0 - win + 1 : 0, wlo1 = (win > 0) ? q1 - win + 1 : 0;
+    const int my_wlo = (win > 0) ? my_pos - win + 1 : 0;
+    auto lower = [](int m, int doc_lo, int win_lo) {
+        return (m == CP_MASK_DOC) ? max(doc_lo, win_lo) : (m == CP_MASK_DIAG_CAUSAL ? win_lo : 0);
+    };
+    const SegRange r0 = key_tile_range<kBN>(mk0, q0, q1, lower(mk0, lo0, wlo0), pos0, len0);
+    const SegRange r1 = key_tile_range<kBN>(mk1, q0, q1, lower(mk1, lo0, wlo0), pos1, len1);
     const int tlo0 = r0.t_lo, thi0 = r0.t_hi, tlo1 = r1.t_lo, thi1 = r1.t_hi;
     // tiles of each segment that need no element mask
-    const SegRange f0r = full_tile_range<kBN>(mk0, q0, mk0 == CP_MASK_DOC ? lo1 : 0, pos0, len0);
-    const SegRange f1r = full_tile_range<kBN>(mk1, q0, mk1 == CP_MASK_DOC ? lo1 : 0, pos1, len1);
+    const SegRange f0r = full_tile_range<kBN>(mk0, q0, lower(mk0, lo1, wlo1), pos0, len0);
+    const SegRange f1r = full_tile_range<kBN>(mk1, q0, lower(mk1, lo1, wlo1), pos1, len1);
+    const int my_lo_doc = max(my_lo, my_wlo);  // this row's lower bound on DOC pairs
     const int flo0 = f0r.t_lo, fn0 = f0r.t_hi - f0r.t_lo;
     const int flo1 = f1r.t_lo, fn1 = f1r.t_hi - f1r.t_lo;
 
@@ -178,7 +189,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
             const int m = sec ? mk1 : mk0;
             uint8_t c = CP_TILE_SKIP;
             if (t >= (sec ? tlo1 : tlo0) && t < (sec ? thi1 : thi0))
-                c = key_tile_full<kBN>(m, q0, m == CP_MASK_DOC ? lo1 : 0, sec ? pos1 : pos0, sec ? len1 : len0, t)
+                c = key_tile_full<kBN>(m, q0, lower(m, lo1, wlo1), sec ? pos1 : pos0, sec ? len1 : len0, t)
                         ? CP_TILE_FULL
                         : CP_TILE_PARTIAL;
             p.tile_map[(int64_t)qt * p.n_ktiles + col] = c;
@@ -278,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         int lo_lim = 0;
         if (ti.mask != CP_MASK_FULL) {
             hi_lim = min(hi_lim, my_pos - ti.kp0);
-            if (ti.mask == CP_MASK_DOC) lo_lim = max(0, my_lo - ti.kp0);
+            lo_lim = max(0, pick(ti.mask == CP_MASK_DOC, my_lo_doc, my_wlo) - ti.kp0);
         }
         const int lo_l = lo_lim - 4 * hl;
         const unsigned span = (unsigned)(hi_lim - lo_lim);
@@ -607,6 +618,7 @@ cp_status fwd_step(const cp_attn_problem* p, const void* q, const void* k, const
     prm.clk = g_clock_buf.load();
     prm.clk_wgs = int32_t(std::min<int64_t>(g_clock_cap.load() / 4, int64_t(1) << 30));
     prm.n_docs = p->n_docs;
+    prm.window = p->window;
     prm.hq = p->hq;
     prm.hkv = p->hkv;
     prm.group = p->hq / p->hkv;

@@ -53,6 +53,7 @@ cp_status validate_problem(const cp_attn_problem* p, bool device_docs) {
         return fail(CP_ERR_INVALID_ARG, "row counts must be in [0, 2^31)");
     if (p->n_q_seg < 1 || p->n_q_seg > 2 || p->n_kv_seg < 1 || p->n_kv_seg > 2)
         return fail(CP_ERR_INVALID_ARG, "segment counts must be 1 or 2");
+    if (p->window < 0) return fail(CP_ERR_INVALID_ARG, "window must be >= 0");
     bool any_doc = false;
     for (int i = 0; i < p->n_q_seg; ++i) {
         const cp_segment& s = p->q_seg[i];
@@ -95,6 +96,13 @@ cp_status validate_problem(const cp_attn_problem* p, bool device_docs) {
         }
     }
     return CP_OK;
+}
+
+int64_t row_lower_bound(const cp_attn_problem* p, int mask, int64_t q) {
+    int64_t lo = kNoLowerBound;
+    if (mask == CP_MASK_DOC) lo = doc_start_host(p->cu_seqlens, p->n_docs, q);
+    if (p->window > 0 && (mask == CP_MASK_DOC || mask == CP_MASK_DIAG_CAUSAL)) lo = std::max(lo, q - p->window + 1);
+    return lo;
 }
 
 TileRange tile_range(int mask, int64_t q0, int64_t q1, int64_t lo0, int64_t kpos0, int64_t klen, int bn) {
@@ -186,6 +194,36 @@ cp_status cp_step_masks(int32_t cp_size, int32_t rank, int32_t step, int32_t pac
     return CP_OK;
 }
 
+cp_status cp_step_masks_window(int64_t seq_len, int32_t cp_size, int32_t rank, int32_t step, int32_t packed,
+                               int64_t window, int32_t mask_out[4]) {
+    int32_t src = 0;
+    cp_status st = cp_ring_source(cp_size, rank, step, &src);
+    if (st != CP_OK) return st;
+    if (!mask_out) return fail(CP_ERR_INVALID_ARG, "mask_out is NULL");
+    if (window < 0) return fail(CP_ERR_INVALID_ARG, "window must be >= 0");
+    if (seq_len <= 0 || seq_len % (2 * int64_t(cp_size)))
+        return fail(CP_ERR_INVALID_ARG, "seq_len must be a positive multiple of 2*cp_size");
+    const int64_t c = seq_len / (2 * int64_t(cp_size));
+    const int64_t qchunk[2] = {rank, 2 * int64_t(cp_size) - 1 - rank};
+    const int64_t kchunk[2] = {src, 2 * int64_t(cp_size) - 1 - src};
+    for (int i = 0; i < 2; ++i) {
+        for (int j = 0; j < 2; ++j) {
+            const int64_t gap = qchunk[i] - kchunk[j];
+            int32_t m;
+            if (gap < 0 || (window > 0 && (gap - 1) * c + 1 >= window))
+                m = CP_MASK_SKIP;  // above the diagonal, or even the closest pair is out of the window
+            else if (packed)
+                m = CP_MASK_DOC;
+            else if (gap > 0 && (window == 0 || (gap + 1) * c - 1 < window))
+                m = CP_MASK_FULL;  // strictly below the diagonal and the farthest pair in the window
+            else
+                m = CP_MASK_DIAG_CAUSAL;
+            mask_out[2 * i + j] = m;
+        }
+    }
+    return CP_OK;
+}
+
 cp_status cp_tile_shape(int32_t hq, int32_t hkv, int32_t head_dim, int32_t* bm_out, int32_t* bn_out) {
     if (!bm_out || !bn_out) return fail(CP_ERR_INVALID_ARG, "output pointer is NULL");
     if (hq <= 0 || hkv <= 0 || hq % hkv) return fail(CP_ERR_INVALID_ARG, "bad head counts");
@@ -227,9 +265,8 @@ cp_status cp_block_map(const cp_attn_problem* p, uint8_t* map_out) {
             for (int j = 0; j < p->n_kv_seg; ++j) {
                 const cp_segment& ks = p->kv_seg[j];
                 const int m = p->mask[i][j];
-                const bool doc = (m == CP_MASK_DOC);
-                const int64_t lo0 = doc ? doc_start_host(p->cu_seqlens, p->n_docs, q0) : kNoLowerBound;
-                const int64_t lo1 = doc ? doc_start_host(p->cu_seqlens, p->n_docs, q1) : kNoLowerBound;
+                const int64_t lo0 = row_lower_bound(p, m, q0);
+                const int64_t lo1 = row_lower_bound(p, m, q1);
                 const int64_t nkt = ceil_div(ks.len, g.bn);
                 TileRange r = tile_range(m, q0, q1, lo0, ks.pos0, ks.len, g.bn);
                 for (int64_t t = 0; t < nkt; ++t) {
@@ -263,8 +300,7 @@ cp_status cp_count_pairs(const cp_attn_problem* p, int64_t* pairs_out) {
             const int64_t kend = ks.pos0 + ks.len;  // exclusive
             for (int64_t r = 0; r < qs.len; ++r) {
                 const int64_t q = qs.pos0 + r;
-                int64_t lo = ks.pos0;
-                if (m == CP_MASK_DOC) lo = std::max(lo, doc_start_host(p->cu_seqlens, p->n_docs, q));
+                const int64_t lo = std::max(ks.pos0, row_lower_bound(p, m, q));
                 const int64_t hi = std::min(kend, q + 1);  // exclusive
                 if (hi > lo) total += hi - lo;
             }

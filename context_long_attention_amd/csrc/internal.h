@@ -50,7 +50,7 @@ inline bool kv_spans_fit(const cp_attn_problem* p) {
 // code) the forward kernel.  For a query tile [q0, q1] (global positions, q1
 // the last row) and a KV segment starting at kpos0 with klen keys in tiles of
 // bn: visited tiles are [t_lo, t_hi).  lo0 / lo1 are the first visible key
-// position of rows q0 / q1 (document start for DOC, unbounded otherwise).
+// position of rows q0 / q1 (row_lower_bound).
 struct TileRange {
     int64_t t_lo, t_hi;
 };
@@ -60,5 +60,10 @@ int tile_class(int mask, int64_t q0, int64_t q1, int64_t lo1, int64_t kpos0, int
 
 // Document start of a global position (host cu_seqlens).
 int64_t doc_start_host(const int32_t* cu, int32_t n_docs, int64_t pos);
+
+// First visible key position of query position q under a pair's mask: the
+// document start (DOC) and q - window + 1 (sliding window, DIAG_CAUSAL and DOC),
+// whichever is later; unbounded below otherwise.  Non-decreasing in q and <= q.
+int64_t row_lower_bound(const cp_attn_problem* p, int mask, int64_t q);
 
 }  // namespace cpattn

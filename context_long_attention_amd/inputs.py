@@ -15,6 +15,8 @@ Recipe (one rank's share is reproducible without materialising the sequence):
   L = clip(round(exp(N(ln 16384, 1))), 256, 524288) are drawn from
   ``np.random.default_rng(seed)`` until they cover S tokens; the last document
   is cut to fit.
+* Sliding-window layers (the pages' window layers of models such as Gemma) use
+  the same draws; only the visibility changes (window of W tokens).
 """
 from __future__ import annotations
 
@@ -94,6 +96,7 @@ class Workload:
     backward: bool
     packed: bool = False
     input_dtype: str = "bf16"   # "fp32" draws are still cast to bf16 for the kernels
+    window: int = 0             # sliding window in tokens (0: none)
 
     @property
     def chunk(self) -> int:
@@ -123,4 +126,9 @@ WORKLOADS = {
     "llama3_405b_fwd": Workload("llama3_405b_fwd", 1 * M, 16, 128, 8, 128, backward=False),
     "llama3_8b_packed": Workload("llama3_8b_packed", 2 * M, 64, 32, 8, 128, backward=True,
                                  packed=True),
+    # window layers: a window inside one chunk (neighbour blocks only) and one spanning chunks
+    "tiny_window": Workload("tiny_window", 512, 4, 4, 2, 64, backward=True, window=48),
+    "tiny_window_wide": Workload("tiny_window_wide", 512, 4, 4, 2, 64, backward=True, window=150),
+    "llama3_8b_window4k": Workload("llama3_8b_window4k", 128 * K, 8, 32, 8, 128, backward=True,
+                                   window=4 * K),
 }

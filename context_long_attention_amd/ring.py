@@ -75,14 +75,27 @@ class RankRing:
         src = cpattn.cp_ring_source(self.R, self.rank, step) if source is None else source
         qa, qb = self.chunks_of(self.rank)
         ka, kb = self.chunks_of(src)
-        masks = cpattn.cp_step_masks(self.R, self.rank, step, self.packed)
+        masks = self.masks_of_source(src)
         cu_ptr, n_docs = None, 0
         if self.packed:
             cu_ptr = self.cu_host.ctypes.data if host_docs else self.cu_dev.data_ptr()
             n_docs = self.n_docs
         return cpattn.make_problem(w.hq, w.hkv, w.dim, w.scale, 2 * c, 2 * c,
                                    [(0, qa * c, c), (c, qb * c, c)], [(0, ka * c, c), (c, kb * c, c)],
-                                   masks, cu_ptr, n_docs)
+                                   masks, cu_ptr, n_docs, w.window)
+
+    def masks_of_source(self, src: int) -> list[list[int]]:
+        """Chunk-pair classes of the local queries against ``src``'s block (the
+        classes of the ring step at which that block arrives)."""
+        step = (self.rank - src) % self.R
+        return cpattn.cp_step_masks_window(self.w.seq_len, self.R, self.rank, step, self.packed, self.w.window)
+
+    def source_live(self, src: int) -> bool:
+        """Whether the local queries can see anything of ``src``'s block.  With a
+        sliding window no longer than a chunk only the rank's own block and its
+        ring neighbours' are live: the short exchange between neighbouring chips
+        of window layers ("Announcing Long-Context Training ...", closing section)."""
+        return any(m != cpattn.CP_MASK_SKIP for row in self.masks_of_source(src) for m in row)
 
     def step_pairs(self, step: int) -> int:
         """Visible (query, key) pairs per query head at ``step`` (host count)."""
@@ -117,9 +130,13 @@ class RankRing:
             lse_acc = torch.full((w.hq, rows), float("-inf"), dtype=torch.float32, device=dev)
             o_t = torch.empty_like(o_acc)
             lse_t = torch.empty_like(lse_acc)
-        feeder = _Feeder(kv_of_source, sched, stage, dev)
-        for t, src in enumerate(sched):
-            k, v = feeder.get(t, compute)
+        # steps with no visible pair are neither received nor computed (their
+        # partial is the merge identity); step 0 (the diagonal) is always live
+        live = [t for t in range(len(sched)) if keep_steps or t == 0 or self.source_live(sched[t])]
+        feeder = _Feeder(kv_of_source, [sched[t] for t in live], stage, dev)
+        for i, t in enumerate(live):
+            src = sched[t]
+            k, v = feeder.get(i, compute)
             p = self.problem(t, src)
             if timer:
                 timer(t, "fwd_begin", compute)
@@ -131,7 +148,7 @@ class RankRing:
                 cpattn.cp_attn_fwd_step_merge(p, q, k, v, o_acc, lse_acc, stream=compute)
             if timer:
                 timer(t, "fwd_end", compute)
-            feeder.release(t, compute)
+            feeder.release(i, compute)
             if not fused:
                 if keep_steps:
                     steps.append((o_t.clone(), lse_t.clone()))
@@ -156,10 +173,19 @@ class RankRing:
         cpattn.cp_attn_bwd_prep(d_o, o, delta, rows, w.hq, w.dim, stream=compute)
         dq = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
         out = []
-        feeder = _Feeder(kv_of_source, sched, stage, dev)
+        # as in the forward: steps with no visible pair are skipped (their dK/dV
+        # are zero; with keep_steps they are returned as zeros)
+        live = [t for t in range(len(sched)) if t == 0 or self.source_live(sched[t])]
+        feeder = _Feeder(kv_of_source, [sched[t] for t in live], stage, dev)
         dk = dv = None
         for t, src in enumerate(sched):
-            k, v = feeder.get(t, compute)
+            if t not in live:
+                if keep_steps:
+                    z = torch.zeros((rows, w.hkv, w.dim), dtype=torch.float32, device=dev)
+                    out.append((src, z, torch.zeros_like(z)))
+                continue
+            i = live.index(t)
+            k, v = feeder.get(i, compute)
             if keep_steps or dk is None:
                 dk = torch.empty((rows, w.hkv, w.dim), dtype=torch.float32, device=dev)
                 dv = torch.empty_like(dk)
@@ -169,7 +195,7 @@ class RankRing:
             cpattn.cp_attn_bwd_step(p, q, k, v, d_o, lse, delta, dq, dk, dv, stream=compute)
             if timer:
                 timer(t, "bwd_end", compute)
-            feeder.release(t, compute)
+            feeder.release(i, compute)
             out.append((src, dk, dv))
         return dq, out
 

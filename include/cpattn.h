@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 2
+#define CPATTN_ABI_VERSION 3
 
 typedef enum cp_status {
     CP_OK = 0,
@@ -54,8 +54,9 @@ typedef enum cp_status {
 /* Class of one (query chunk, key chunk) pair of a ring step. */
 typedef enum cp_mask {
     CP_MASK_FULL = 0,        /* every key visible to every query: no element mask */
-    CP_MASK_DIAG_CAUSAL = 1, /* key visible iff key position <= query position */
-    CP_MASK_DOC = 2,         /* causal and inside the same packed document */
+    CP_MASK_DIAG_CAUSAL = 1, /* key visible iff key position <= query position
+                                (and inside the sliding window, if any) */
+    CP_MASK_DOC = 2,         /* DIAG_CAUSAL and inside the same packed document */
     CP_MASK_SKIP = 3         /* nothing visible: the pair is not computed */
 } cp_mask;
 
@@ -77,7 +78,14 @@ typedef struct cp_segment {
  * segments (the source rank's two chunks).  Query segments must not share
  * rows.  mask[i][j] is the class of (query segment i, KV segment j); the
  * kernels trust FULL and SKIP and apply element masks only on partially
- * visible tiles of DIAG_CAUSAL and DOC pairs. */
+ * visible tiles of DIAG_CAUSAL and DOC pairs.
+ *
+ * Sliding window ("Announcing Long-Context Training ...", closing section:
+ * models such as Gemma mix sliding-window layers with global ones): with
+ * window = W > 0, a DIAG_CAUSAL or DOC pair sees key k from query q only if
+ * q - W < k <= q (the W most recent positions, q itself included).  A pair
+ * the window cuts must not be marked FULL: cp_step_masks_window classifies
+ * ring steps accordingly.  window = 0: no window. */
 typedef struct cp_attn_problem {
     int32_t hq, hkv, head_dim;
     float scale;              /* softmax scale, normally 1/sqrt(head_dim) */
@@ -93,6 +101,7 @@ typedef struct cp_attn_problem {
      * pointer for cp_block_map and cp_count_pairs. */
     const int32_t* cu_seqlens;
     int32_t n_docs;
+    int32_t window;           /* sliding window in tokens, 0 = none (>= 0) */
 } cp_attn_problem;
 
 /* ---------------------------------------------------------------- host ---- */
@@ -122,6 +131,21 @@ cp_status cp_ring_source(int32_t cp_size, int32_t rank, int32_t step, int32_t* s
  * query gives FULL / DIAG_CAUSAL / SKIP.  packed != 0: every non-SKIP pair is
  * DOC (document boundaries may fall anywhere). */
 cp_status cp_step_masks(int32_t cp_size, int32_t rank, int32_t step, int32_t packed, int32_t mask_out[4]);
+
+/* Chunk-pair classes of step t for rank r in a layer with a sliding window of
+ * `window` tokens (0 = none, which gives cp_step_masks), for a sequence of
+ * seq_len tokens (chunks of c = seq_len / (2*cp_size)).  A pair (query chunk
+ * I, key chunk J) is SKIP when J > I or when its closest pair is at least
+ * `window` positions apart ((I-J-1)*c + 1 >= window), FULL when J < I and
+ * its farthest pair is inside the window ((I-J+1)*c - 1 < window, or no
+ * window), DIAG_CAUSAL otherwise; packed != 0 turns every non-SKIP class into
+ * DOC.  With window <= c only the rank's own block and its ring neighbours'
+ * (steps 0, 1 and cp_size-1) have any visible pair: the short exchange between
+ * neighbouring chips the pages describe for window layers.
+ * INVALID_ARG as cp_step_masks, or for seq_len not a positive multiple of
+ * 2*cp_size or window < 0. */
+cp_status cp_step_masks_window(int64_t seq_len, int32_t cp_size, int32_t rank, int32_t step, int32_t packed,
+                               int64_t window, int32_t mask_out[4]);
 
 /* Tile shape of the forward kernel for this head configuration: bm query rows
  * x bn keys.  The block map and tile_map_out use this shape.  UNSUPPORTED for

@@ -179,3 +179,96 @@ def test_schedule_check_rejects_dropped_or_repeated_steps():
     assert ring.schedule() == [oracle.ring_source(1, t, 4) for t in range(4)]
     with pytest.raises(RingScheduleError):
         ring.forward(None, None, schedule=[1, 0, 0, 2])
+
+
+# ------------------------------------------------------------------ sliding window
+@pytest.mark.parametrize("S,R", [(16, 2), (48, 3), (64, 4), (80, 5), (512, 4)])
+def test_window_step_masks_match_brute_force(S, R):
+    """cp_step_masks_window's closed form against the oracle's brute-force classes for
+    windows inside a chunk, across chunks, exactly at chunk multiples and beyond."""
+    c = S // (2 * R)
+    cu = np.array([0, 3, 3, S // 2 + 1, S], dtype=np.int32)
+    windows = sorted({1, 2, c - 1, c, c + 1, 2 * c - 1, 2 * c, 2 * c + 1, 3 * c, S, 0} - {-1})
+    for wdw in windows:
+        if wdw < 0:
+            continue
+        for r in range(R):
+            qpos = oracle.zigzag_positions(S, R, r)
+            for t in range(R):
+                kpos = oracle.zigzag_positions(S, R, oracle.ring_source(r, t, R))
+                for packed in (False, True):
+                    got = cpattn.cp_step_masks_window(S, R, r, t, packed, wdw)
+                    for i in range(2):
+                        for j in range(2):
+                            ref = oracle.chunk_pair_class(qpos[i * c:(i + 1) * c], kpos[j * c:(j + 1) * c],
+                                                          cu if packed else None, wdw)
+                            if packed and ref == oracle.CLS_SKIP:
+                                assert got[i][j] in (oracle.CLS_SKIP, oracle.CLS_DOC)
+                            else:
+                                assert got[i][j] == ref, (wdw, r, t, i, j, packed)
+    # window 0 is the plain causal classification
+    for r in range(R):
+        for t in range(R):
+            assert cpattn.cp_step_masks_window(S, R, r, t, False, 0) == cpattn.cp_step_masks(R, r, t, False)
+
+
+WINDOW_MAP_CASES = [
+    # S, R, Hq, Hkv, D, packed, window
+    (400, 2, 8, 2, 128, False, 37),
+    (462, 3, 4, 4, 64, False, 77),
+    (462, 3, 4, 4, 64, False, 100),
+    (360, 2, 6, 3, 128, True, 50),
+    (1024, 4, 8, 2, 128, False, 128),
+    (1024, 4, 8, 2, 128, True, 300),
+]
+
+
+@pytest.mark.parametrize("S,R,hq,hkv,d,packed,window", WINDOW_MAP_CASES)
+def test_window_block_map_and_pairs_match_brute_force(S, R, hq, hkv, d, packed, window):
+    cu = None
+    if packed:
+        cu = np.array([0, 1, 2, S // 3, S // 3 + 1, S // 2, S - 1, S], dtype=np.int32)
+    w = inputs.Workload("case", S, R, hq, hkv, d, backward=False, packed=packed, window=window)
+    bm, bn = cpattn.cp_tile_shape(hq, hkv, d)
+    for r in range(R):
+        ring = RankRing(w, r, cu, device="cpu")
+        for t in range(R):
+            src = ring.schedule()[t]
+            p = ring.problem(t, host_docs=True)
+            assert p.window == window
+            qseg = [(int(p.q_seg[i].pos0), int(p.q_seg[i].len)) for i in range(p.n_q_seg)]
+            kseg = [(int(p.kv_seg[j].pos0), int(p.kv_seg[j].len)) for j in range(p.n_kv_seg)]
+            ref = oracle.tile_map(qseg, kseg, bm, bn, cu, window)
+            assert np.array_equal(cpattn.cp_block_map(p), ref), (r, t)
+            kpos = cpattn.cp_partition_zigzag(S, R, src)
+            vis = oracle.visibility(ring.pos, kpos, cu, window)
+            assert cpattn.cp_count_pairs(p) == int(vis.sum())
+            if packed:  # document boundaries are not known to the chunk classes: live is conservative
+                assert ring.source_live(src) or not vis.any()
+            else:
+                assert ring.source_live(src) == bool(vis.any()) or t == 0
+
+
+def test_window_validation():
+    F = cpattn.CP_MASK_FULL
+    p = cpattn.make_problem(4, 2, 128, 0.1, 64, 64, [(0, 0, 64)], [(0, 0, 64)], [[F, F], [F, F]], window=-1)
+    with pytest.raises(cpattn.CpError) as e:
+        cpattn.cp_count_pairs(p)
+    assert e.value.status == cpattn.CP_ERR_INVALID_ARG
+    with pytest.raises(cpattn.CpError):
+        cpattn.cp_step_masks_window(64, 4, 0, 0, False, -5)
+    with pytest.raises(cpattn.CpError):
+        cpattn.cp_step_masks_window(60, 4, 0, 0, False, 5)
+
+
+def test_ring_masks_follow_the_block_not_the_step():
+    """problem(t, src) classifies against the block actually passed: a permuted but
+    complete schedule gets the classes of each block's own arrival step."""
+    w = inputs.Workload("perm", 64, 4, 4, 2, 64, backward=False, window=12)
+    ring = RankRing(w, 1, device="cpu")
+    for src in range(4):
+        natural = (1 - src) % 4
+        for t in range(4):
+            p = ring.problem(t, src, host_docs=True)
+            assert [[p.mask[i][j] for j in range(2)] for i in range(2)] == \
+                cpattn.cp_step_masks_window(64, 4, 1, natural, False, 12)
