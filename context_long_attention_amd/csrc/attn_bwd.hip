@@ -28,6 +28,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 #include "tiles.h"
@@ -111,6 +112,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     const int key_row0 = p.ks_row0[s] + kt_in * BK;
     const int kpos0 = p.ks_pos0[s] + kt_in * BK;
     const int kcount = min(BK, p.ks_len[s] - kt_in * BK);
+    // query-segment parameters as opaque scalars, selected by value below (an
+    // index into the parameter block would be a scalar memory load, whose wait
+    // also drains the LDS counter, at every use)
+    const int qlen_a = sreg(p.qs_len[0]), qlen_b = sreg(p.qs_len[1]);
+    const int qrow_a = sreg(p.qs_row0[0]), qrow_b = sreg(p.qs_row0[1]);
+    const int qpos_a = sreg(p.qs_pos0[0]), qpos_b = sreg(p.qs_pos0[1]);
+    const int mq_a = sreg(s ? p.mask[0][1] : p.mask[0][0]), mq_b = sreg(s ? p.mask[1][1] : p.mask[1][0]);
     const int k0p = kpos0, k1p = kpos0 + kcount - 1;
     const int kk = 32 * wave + ql;  // this lane's key within the tile
     const bool key_valid = kk < kcount;
@@ -199,8 +207,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     auto issue = [&](int it, char* qdst, char* odst, char* adst) {
         const Item x = item_of(it);
         const bool live = it < n_it;
-        const int rows = live ? min(BQ, p.qs_len[x.qs] - x.tq * BQ) : 0;
-        const int row0 = p.qs_row0[x.qs] + x.tq * BQ;
+        const int rows = live ? min(BQ, pick(x.qs != 0, qlen_b, qlen_a) - x.tq * BQ) : 0;
+        const int row0 = pick(x.qs != 0, qrow_b, qrow_a) + x.tq * BQ;
         const int64_t off = ((int64_t)row0 * p.hq + x.head) * D;
         load_tile_lds<D, BQ, kKvWaves>(qdst, tile_rsrc(p.q + off, rows, qrow_bytes), qrow_bytes, wave, lane);
         load_tile_lds<D, BQ, kKvWaves>(odst, tile_rsrc(p.d_o + off, rows, qrow_bytes), qrow_bytes, wave, lane);
@@ -225,9 +233,9 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
                     char* afill) {
         issue(it + 3, qfill, ofill, afill);
         const Item x = item_of(it);
-        const int m = p.mask[x.qs][s];
-        const int qrows = min(BQ, p.qs_len[x.qs] - x.tq * BQ);
-        const int qpos0 = p.qs_pos0[x.qs] + x.tq * BQ;
+        const int m = pick(x.qs != 0, mq_b, mq_a);
+        const int qrows = min(BQ, pick(x.qs != 0, qlen_b, qlen_a) - x.tq * BQ);
+        const int qpos0 = pick(x.qs != 0, qpos_b, qpos_a) + x.tq * BQ;
 
         // S = Q K^T and dP = dO V^T: 32 queries x this wave's 32 keys
         f32x16 sc = f32x16{}, dp = f32x16{};
@@ -252,17 +260,22 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
         f32x16 pr, dsr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int q4 = 8 * i + 4 * hl;
-            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_row + q4);
-            const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_row + q4);
+            const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse_row + 8 * i + 4 * hl);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 4 * i + j;
-                float pv = __builtin_amdgcn_exp2f(fmaf(sc[r], c2, -l4[j] * kLog2e));
-                if (!full && (unsigned)(qk + 8 * i + j) >= span) pv = 0.f;
-                pr[r] = pv;
-                dsr[r] = pv * (dp[r] - d4[j]);
-            }
+            for (int j = 0; j < 4; ++j) pr[4 * i + j] = __builtin_amdgcn_exp2f(fmaf(sc[4 * i + j], c2, -l4[j] * kLog2e));
+        }
+        if (!full) {  // element mask on partial tiles only (a wave-uniform branch)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if ((unsigned)(qk + 8 * i + j) >= span) pr[4 * i + j] = 0.f;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_row + 8 * i + 4 * hl);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) dsr[4 * i + j] = pr[4 * i + j] * (dp[4 * i + j] - d4[j]);
         }
         bf16x8 pb[2], sb[2];
 #pragma unroll
@@ -463,8 +476,7 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
     const int t_lane = L::off(4 * (grp >> 1) + (jl >> 2), 16 * (grp & 1) + 4 * (jl & 3));
     constexpr int kPending = 2 * 2 * (L::NBLK / kQWaves);
 
-    auto step = [&](int it, const char* ksl, const char* vsl, char* kfill, char* vfill) {
-        issue(it + 3, kfill, vfill);
+    auto step = [&](auto bar, int it, const char* ksl, const char* vsl, char* kfill, char* vfill) {
         const TileRef tr = tile_of(it);
         // S^T = K Q^T and dP^T = V dO^T: 64 keys x this wave's 32 queries
         f32x16 sc[2], dp[2];
@@ -476,6 +488,13 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
             for (int ds = 0; ds < DS; ++ds) {
                 const bf16x8 a = *reinterpret_cast<const bf16x8*>(ksl + k_lane + L::off(32 * kb, 16 * ds));
                 sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ds], sc[kb], 0, 0, 0);
+                if (kb == 0 && ds == 3) {
+                    // this step's loads, a few MFMAs in: their address arithmetic is
+                    // off the path from the barrier to the first MFMA
+                    order_memory();
+                    issue(it + 2, kfill, vfill);
+                    order_memory();
+                }
             }
 #pragma unroll
             for (int ds = 0; ds < DS; ++ds) {
@@ -507,17 +526,23 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
         // P = exp2(c2 s - log2e LSE), dS = P (dP - delta), rounded to bf16 for dQ
         bf16x8 sb[4];
 #pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sc[kb][r] = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c2, nl));
+        if (!vis_all) {  // element mask on partial or ragged tiles only (a wave-uniform branch)
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (none || (unsigned)(row_of_reg(kb, r, 0) - lo_l) > span) sc[kb][r] = 0.f;
+        }
+#pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
             for (int half = 0; half < 2; ++half) {
                 f32x8 v8;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int r = 8 * half + e;
-                    float pv = __builtin_amdgcn_exp2f(fmaf(sc[kb][r], c2, nl));
-                    if (!vis_all && (none || (unsigned)(row_of_reg(kb, r, 0) - lo_l) > span)) pv = 0.f;
-                    v8[e] = pv * (dp[kb][r] - dl);
-                }
+                for (int e = 0; e < 8; ++e) v8[e] = sc[kb][8 * half + e] * (dp[kb][8 * half + e] - dl);
                 sb[2 * kb + half] = __builtin_convertvector(v8, bf16x8);
             }
         }
@@ -534,19 +559,24 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
                                                                    0, 0, 0);
             }
         }
-        ring_barrier<kPending>();
+        if constexpr (decltype(bar)::value) ring_barrier<0>();
     };
 
+    // Step s reads tile s (slot s mod 4) and fills slot (s+2) mod 4, last read at
+    // step s-2, before the last barrier; a barrier after every odd step first
+    // waits for all of the wave's loads, so the two tiles the next two steps
+    // read have landed.
     if (n_it > 0) {
         issue(0, kb0, vb0);
         issue(1, kb1, vb1);
-        issue(2, kb2, vb2);
-        ring_barrier<kPending>();  // tile 0 has landed
+        ring_barrier<0>();  // tiles 0 and 1 have landed
+        using NoBar = std::integral_constant<bool, false>;
+        using Bar = std::integral_constant<bool, true>;
         for (int it = 0; it < n_it; it += 4) {
-            step(it, kb0, vb0, kb3, vb3);
-            if (it + 1 < n_it) step(it + 1, kb1, vb1, kb0, vb0);
-            if (it + 2 < n_it) step(it + 2, kb2, vb2, kb1, vb1);
-            if (it + 3 < n_it) step(it + 3, kb3, vb3, kb2, vb2);
+            step(NoBar{}, it, kb0, vb0, kb2, vb2);
+            if (it + 1 < n_it) step(Bar{}, it + 1, kb1, vb1, kb3, vb3);
+            if (it + 2 < n_it) step(NoBar{}, it + 2, kb2, vb2, kb0, vb0);
+            if (it + 3 < n_it) step(Bar{}, it + 3, kb3, vb3, kb1, vb1);
         }
     }
 

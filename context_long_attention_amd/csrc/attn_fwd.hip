@@ -16,8 +16,8 @@
 //    operand of O^T += V^T P^T; V stays row-major in LDS and its transposed
 //    operand comes from the transposing LDS read (ds_read_tr16_b64).
 //  * K/V tiles move HBM -> LDS with direct buffer loads (rows past a ragged
-//    tile read as zero) into a ring of four K and four V buffers, three tiles
-//    ahead of use; each step waits only for the tiles the next step reads.
+//    tile read as zero) into a ring of four K and four V buffers, two tiles
+//    ahead of use, with one workgroup barrier every second tile.
 //  * Rotated pipeline: one step alternates the MFMAs of the P V product of
 //    tile i-1 and of the scores of tile i+1, with the exponentials, row sum and
 //    bf16 convert of tile i spread over them.
@@ -38,6 +38,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "internal.h"
 #include "tiles.h"
@@ -273,10 +274,6 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
             }
     };
 
-    // At each step's barrier the loads of the last two steps may still be in
-    // flight; everything older (the tiles the next step reads) has landed.
-    constexpr int kPending = 2 * 2 * (L::NBLK / kWaves);
-
     bf16x8 pa[4], pbb[4];  // P (bf16) of two consecutive tiles: one being made, one consumed by P V
 
     // Element mask of tile it's scores on partial or ragged tiles: key k of the
@@ -428,15 +425,19 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
 
     // Pipeline step it (1 <= it < n_it):
     //   mask of tile it (partial tiles only);
-    //   loads (issued after the fourth MFMA): K(it+4) into the K slot freed by
-    //   K(it), V(it+2) into the V slot freed by V(it-2);
+    //   loads (issued after the fourth MFMA): K(it+3) and V(it+1);
     //   32 MFMAs alternating O^T += V(it-1)^T P(it-1) and the scores of tile it+1,
     //   with the exponential, bf16 convert and row sum of one score of tile it
     //   after each (P(it) into p_new);
     //   the slow-path check of tile it.
+    //   a barrier after every second step (even it), when bar is true.
     // Slots: K(j) and V(j) live in slot j mod 4, so each unrolled copy below
-    // touches statically known buffers.
-    auto step = [&](int it, f32x16* cur, f32x16* nxt, const bf16x8* p_old, bf16x8* p_new, char* k_fill,
+    // touches statically known buffers.  Step s reads K(s+1) and V(s-1) and
+    // fills the slots of K(s-1) and V(s-3), whose last reads were at steps s-2
+    // and earlier, before the last barrier (after step s-1 or s-2).  Every
+    // barrier first waits for all of the wave's loads, so the tiles the next two
+    // steps read (issued in the two steps before the barrier) have landed.
+    auto step = [&](auto bar, int it, f32x16* cur, f32x16* nxt, const bf16x8* p_old, bf16x8* p_new, char* k_fill,
                     const char* k_read, char* v_fill, const char* v_read) {
         mask_tile(it, cur);
         lds_char* vbase = lds_base(v_read, v_lane);
@@ -473,8 +474,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
             if (j == 3) {
                 // this step's loads, issued a few MFMAs in so that their address
                 // arithmetic is off the path from the barrier to the first MFMA
-                issue(false, it + 4, k_fill);
-                issue(true, it + 2, v_fill);
+                issue(false, it + 3, k_fill);
+                issue(true, it + 1, v_fill);
                 order_memory();
             }
             // scores e of this lane (register e % 16 of block e / 16)
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         }
         pack_p(pbits, p_new);
         l_run += check_tile(cur, p_new, sa + sb);
-        ring_barrier<kPending>();  // the tiles the next step reads have landed; this step's slots are free
+        if constexpr (decltype(bar)::value) ring_barrier<0>();
     };
 
     f32x16 sa[2], sb[2];
@@ -506,24 +507,22 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         issue(false, 1, kb1);
         __syncthreads();
         scores(kb0, sa);
-        // issue order matters for the wait counts: V0, K2, V1, K3, then two per step
-        issue(true, 0, vb0);
         issue(false, 2, kb2);
-        issue(true, 1, vb1);
-        issue(false, 3, kb3);
-        ring_barrier<kPending>();  // every wave has read K(0), so its slot can be refilled
+        issue(true, 0, vb0);
         // step 0: no P V yet; tile 0's maximum sets the reference
-        issue(false, 4, kb0);
-        issue(true, 2, vb2);
+        issue(false, 3, kb3);
+        issue(true, 1, vb1);
         mask_tile(0, sa);
         raise_max(tile_max2(sa));
         l_run += scores_and_exp(kb1, sa, sb, pa);
-        ring_barrier<kPending>();
+        ring_barrier<0>();
+        using NoBar = std::integral_constant<bool, false>;
+        using Bar = std::integral_constant<bool, true>;
         for (int it = 1; it < n_it; it += 4) {
-            step(it, sb, sa, pa, pbb, kb1, kb2, vb3, vb0);
-            if (it + 1 < n_it) step(it + 1, sa, sb, pbb, pa, kb2, kb3, vb0, vb1);
-            if (it + 2 < n_it) step(it + 2, sb, sa, pa, pbb, kb3, kb0, vb1, vb2);
-            if (it + 3 < n_it) step(it + 3, sa, sb, pbb, pa, kb0, kb1, vb2, vb3);
+            step(NoBar{}, it, sb, sa, pa, pbb, kb0, kb2, vb2, vb0);
+            if (it + 1 < n_it) step(Bar{}, it + 1, sa, sb, pbb, pa, kb1, kb3, vb3, vb1);
+            if (it + 2 < n_it) step(NoBar{}, it + 2, sb, sa, pa, pbb, kb2, kb0, vb0, vb2);
+            if (it + 3 < n_it) step(Bar{}, it + 3, sa, sb, pbb, pa, kb3, kb1, vb1, vb3);
         }
         // the last P V: V(n_it - 1) landed at the last step's barrier; P(j)
         // lives in pa for even j and in pbb for odd j
