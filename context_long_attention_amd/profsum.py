@@ -1,6 +1,6 @@
 """Short text summaries of rocprofv3 CSV output, and the traffic lookup bench.py uses.
 
-Two summaries are produced (both are markdown with the exact commands that made
+Three summaries are produced (all markdown with the exact commands that made
 them):
 
 * ``stats``: the per-kernel table of a ``rocprofv3 --kernel-trace --stats
@@ -12,6 +12,8 @@ them):
   result is in bytes of memory traffic per launch.  The summary records a
   SHA-256 of the kernel's source files; ``read_traffic`` returns the figure
   only while those sources are unchanged.
+* ``counters``: MFMA utilisation and instruction mix per kernel from one
+  ``--pmc`` pass over the SQ counters listed in ``SQ_COUNTERS``.
 
 Usage::
 
@@ -200,6 +202,49 @@ def read_traffic(path: str, kernel: str, workload: str):
     return t
 
 
+# Counters of the MFMA-utilisation summary (one rocprofv3 --pmc pass: 8 SQ and 1 GRBM counters).
+SQ_COUNTERS = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+               "SQ_LDS_BANK_CONFLICT", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "GRBM_GUI_ACTIVE"]
+N_XCD, N_SIMD = 8, 1024  # MI355X: GRBM_GUI_ACTIVE sums the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def counters(path: str):
+    """Per kernel: launches and the per-launch average of every counter in SQ_COUNTERS."""
+    per = defaultdict(lambda: defaultdict(float))
+    names = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = int(r["Dispatch_Id"])
+            per[d][r["Counter_Name"]] += float(r["Counter_Value"])
+            names[d] = short_name(r["Kernel_Name"])
+    out = defaultdict(lambda: defaultdict(list))
+    for d, cs in per.items():
+        for c, v in cs.items():
+            out[names[d]][c].append(v)
+    return {k: {"launches": len(next(iter(cs.values()))), **{c: sum(v) / len(v) for c, v in cs.items()}}
+            for k, cs in out.items()}
+
+
+def counters_markdown(path: str, commands, kernels, title: str) -> str:
+    cs = counters(path)
+    out = [f"# {title}", "", "Made by:", "", "```", *commands, "```", "",
+           "Per launch (average over launches). cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs);",
+           "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); VALU/MFMA counts the non-MFMA vector",
+           "instructions per MFMA; waiting = SQ_WAIT_ANY / SQ_WAVE_CYCLES (waves stalled on a dependency counter).", "",
+           "| kernel | launches | cycles | MFMA busy | MFMAs | VALU/MFMA | LDS/MFMA | LDS bank conflicts | waiting |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for k in kernels:
+        if k not in cs:
+            raise SystemExit(f"kernel {k!r} not in {path} (have {sorted(cs)})")
+        c = cs[k]
+        cyc = c["GRBM_GUI_ACTIVE"] / N_XCD
+        mf = c["SQ_INSTS_MFMA"]
+        out.append(f"| `{k}` | {c['launches']} | {cyc:.4g} | {c['SQ_VALU_MFMA_BUSY_CYCLES'] / (N_SIMD * cyc):.3f} | "
+                   f"{mf:.4g} | {(c['SQ_INSTS_VALU'] - mf) / mf:.2f} | {c['SQ_INSTS_LDS'] / mf:.2f} | "
+                   f"{c['SQ_LDS_BANK_CONFLICT']:.0f} | {c['SQ_WAIT_ANY'] / c['SQ_WAVE_CYCLES']:.2f} |")
+    return "\n".join(out) + "\n"
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -219,9 +264,17 @@ def main(argv=None):
     t.add_argument("--algorithmic-bytes", type=int)
     t.add_argument("--command", action="append", default=[])
     t.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True)
+    c.add_argument("--kernel", action="append", required=True)
+    c.add_argument("--command", action="append", default=[])
+    c.add_argument("--title", default="MFMA utilisation from SQ counters")
+    c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         text = stats_markdown(a.csv, a.command, a.top, a.title)
+    elif a.cmd == "counters":
+        text = counters_markdown(a.csv, a.command, a.kernel, a.title)
     else:
         tr = traffic(a.fetch, a.write, a.kernel, a.copy_mib << 20, a.copy_count)
         text = traffic_markdown(tr, a.workload, a.command, a.algorithmic_bytes)
