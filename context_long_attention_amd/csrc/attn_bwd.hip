@@ -73,8 +73,6 @@ constexpr int BK = kBwdKeysPerWG;  // 128 keys per workgroup
 constexpr int BQ = kBwdQRows;      // 32 query rows per tile
 constexpr int kAuxBytes = 256 * kKvWaves;  // per slot: LSE row, delta row, two dummy areas
 
-template <int D>
-constexpr int kv_loads_per_item() { return 2 * (TileLayout<D, BQ>::NBLK / kKvWaves) + 1; }
 
 template <int D>
 __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams p) {
@@ -227,11 +225,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     const int q_lane = TileLayout<D, BQ>::off(ql, 8 * hl);
     const int grp = lane >> 4, jl = lane & 15;
     const int t_lane = TileLayout<D, BQ>::off(4 * (grp >> 1) + (jl >> 2), 16 * (grp & 1) + 4 * (jl & 3));
-    constexpr int kPending = 2 * kv_loads_per_item<D>();
-
-    auto step = [&](int it, const char* qsl, const char* osl, const char* asl, char* qfill, char* ofill,
+    auto step = [&](auto bar, int it, const char* qsl, const char* osl, const char* asl, char* qfill, char* ofill,
                     char* afill) {
-        issue(it + 3, qfill, ofill, afill);
         const Item x = item_of(it);
         const int m = pick(x.qs != 0, mq_b, mq_a);
         const int qrows = min(BQ, pick(x.qs != 0, qlen_b, qlen_a) - x.tq * BQ);
@@ -248,6 +243,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
         for (int ds = 0; ds < DS; ++ds) {
             const bf16x8 a = *reinterpret_cast<const bf16x8*>(osl + q_lane + L::off(0, 16 * ds));
             dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, vf[ds], dp, 0, 0, 0);
+            if (ds == 1) {
+                order_memory();
+                issue(it + 2, qfill, ofill, afill);
+                order_memory();
+            }
         }
 
         // P = exp2(c2 s - log2e LSE) and dS = P (dP - delta); rows past a ragged tile
@@ -308,19 +308,23 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
                                                                    0, 0, 0);
             }
         }
-        ring_barrier<kPending>();  // item it+1 has landed; this item's slot is free
+        if constexpr (decltype(bar)::value) ring_barrier<0>();
     };
 
+    // Item s reads slot s mod 4 and fills slot (s+2) mod 4, last read by item
+    // s-2, before the last barrier; a barrier after every odd item first waits
+    // for all of the wave's loads, so the next two items have landed.
     if (n_it > 0) {
         issue(0, qt0, ot0, ax0);
         issue(1, qt1, ot1, ax1);
-        issue(2, qt2, ot2, ax2);
-        ring_barrier<kPending>();  // item 0 has landed
+        ring_barrier<0>();  // items 0 and 1 have landed
+        using NoBar = std::integral_constant<bool, false>;
+        using Bar = std::integral_constant<bool, true>;
         for (int it = 0; it < n_it; it += 4) {
-            step(it, qt0, ot0, ax0, qt3, ot3, ax3);
-            if (it + 1 < n_it) step(it + 1, qt1, ot1, ax1, qt0, ot0, ax0);
-            if (it + 2 < n_it) step(it + 2, qt2, ot2, ax2, qt1, ot1, ax1);
-            if (it + 3 < n_it) step(it + 3, qt3, ot3, ax3, qt2, ot2, ax2);
+            step(NoBar{}, it, qt0, ot0, ax0, qt2, ot2, ax2);
+            if (it + 1 < n_it) step(Bar{}, it + 1, qt1, ot1, ax1, qt3, ot3, ax3);
+            if (it + 2 < n_it) step(NoBar{}, it + 2, qt2, ot2, ax2, qt0, ot0, ax0);
+            if (it + 3 < n_it) step(Bar{}, it + 3, qt3, ot3, ax3, qt1, ot1, ax1);
         }
     }
 
@@ -474,7 +478,6 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
     const int k_lane = L::off(ql, 8 * hl);
     const int grp = lane >> 4, jl = lane & 15;
     const int t_lane = L::off(4 * (grp >> 1) + (jl >> 2), 16 * (grp & 1) + 4 * (jl & 3));
-    constexpr int kPending = 2 * 2 * (L::NBLK / kQWaves);
 
     auto step = [&](auto bar, int it, const char* ksl, const char* vsl, char* kfill, char* vfill) {
         const TileRef tr = tile_of(it);
