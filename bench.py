@@ -391,6 +391,29 @@ def measure_window(torch, w, rank, steps, warmup):
             "bwd_kernel_tflops": round(tflops(f_bwd, bwd_timer.total_ms() / steps), 2)}
 
 
+def measure_large(torch, w, rank, steps, warmup):
+    """The Llama-3-405B prefill share: rank 0's whole forward ring (16 steps of
+    64K-token KV blocks), with inputs drawn on the device (only shapes matter for
+    timing; the parity tests use the seeded recipe)."""
+    from context_long_attention_amd.ring import RankRing
+    q = _dev_normal(torch, (w.local, w.hq, w.dim), 1001)
+    kv = {s: (_dev_normal(torch, (w.local, w.hkv, w.dim), 1100 + s), _dev_normal(torch, (w.local, w.hkv, w.dim), 1200 + s))
+          for s in range(w.cp)}
+    ring = RankRing(w, rank)
+    flops = sum(ring.step_pairs(t) for t in range(w.cp)) * w.hq * w.dim * 4
+    timer = KernelTimer(torch, "fwd")
+
+    def one(tm):
+        RankRing(w, rank).forward(q, kv.__getitem__, stage=True, timer=tm)
+
+    ms, kern = _time_leg(torch, one, steps, warmup, timer)
+    log(f"{w.name}: {ms:.1f} ms per ring")
+    return {"workload": f"{w.name}: Hq={w.hq} Hkv={w.hkv} D={w.dim}, rank {rank} of S={w.seq_len} at CP={w.cp}, "
+                        f"{w.cp} ring steps of {w.local}-token KV blocks, fwd",
+            "tflops": round(tflops(flops, ms), 2), "pct_bf16_peak": round(100 * tflops(flops, ms) / BF16_PEAK_TFLOPS, 2),
+            "kernel_tflops": round(tflops(flops, kern), 2), "ms_per_ring": round(ms, 2)}
+
+
 def tflops(flops, ms):
     return flops / (ms * 1e-3) / 1e12
 
@@ -408,6 +431,7 @@ def main():
     ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--no-variants", action="store_true", help="skip the Pass Q / prefill / gathered legs")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window layer leg")
+    ap.add_argument("--no-large", action="store_true", help="skip the Llama-3-405B prefill leg")
     ap.add_argument("--window-workload", default="llama3_8b_window4k")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first make 3 device-to-device copies of this many MiB (counter calibration)")
@@ -481,6 +505,8 @@ def main():
         }
     if not args.no_variants:
         record["variants"] = measure_variants(torch, w, args.rank, max(1, args.steps // 2), 1)
+    if not args.no_large:
+        record["llama3_405b_fwd"] = measure_large(torch, inputs.WORKLOADS["llama3_405b_fwd"], args.rank, 1, 1)
     if not args.no_window:
         record["sliding_window"] = measure_window(torch, inputs.WORKLOADS[args.window_workload], args.rank,
                                                   max(1, args.steps // 2), 1)
