@@ -414,6 +414,44 @@ def measure_large(torch, w, rank, steps, warmup):
             "kernel_tflops": round(tflops(flops, kern), 2), "ms_per_ring": round(ms, 2)}
 
 
+def measure_packed(torch, w, steps, warmup):
+    """The packed-document training workload over all of its ranks: every rank's
+    forward and backward ring over the seeded document layout (block-diagonal
+    causal masks, fully masked tiles and blocks skipped).  Per-rank work varies
+    widely, so the leg times all ranks back to back; FLOPs count only the visible
+    (document-causal) pairs.  Inputs are drawn on the device."""
+    from context_long_attention_amd.ring import RankRing
+    cu = w.cu_seqlens()
+    q = _dev_normal(torch, (w.local, w.hq, w.dim), 2001)
+    d_o = _dev_normal(torch, (w.local, w.hq, w.dim), 2002)
+    kv = {s: (_dev_normal(torch, (w.local, w.hkv, w.dim), 2100 + s), _dev_normal(torch, (w.local, w.hkv, w.dim), 2200 + s))
+          for s in range(w.cp)}
+    rings = [RankRing(w, r, cu) for r in range(w.cp)]
+    pairs = sum(ring.step_pairs(t) for ring in rings for t in range(w.cp))
+    fwd_t, bwd_t = KernelTimer(torch, "fwd"), KernelTimer(torch, "bwd")
+
+    def timer(step, what, stream):
+        fwd_t(step, what, stream)
+        bwd_t(step, what, stream)
+
+    def one(tm):
+        for ring in rings:
+            o, lse, _ = ring.forward(q, kv.__getitem__, stage=True, timer=tm)
+            ring.backward(q, d_o, o, lse, kv.__getitem__, stage=True, keep_steps=False, timer=tm)
+
+    ms, _ = _time_leg(torch, one, steps, warmup, None)
+    fwd_t.enabled = bwd_t.enabled = True
+    one(timer)
+    torch.cuda.synchronize()
+    f_fwd, f_bwd = pairs * w.hq * w.dim * 4, pairs * w.hq * w.dim * 10
+    log(f"{w.name}: {ms:.1f} ms for all {w.cp} ranks")
+    return {"workload": f"{w.name}: S={w.seq_len} at CP={w.cp}, {len(cu) - 1} documents, every rank's fwd+bwd ring",
+            "pairs_per_head": pairs, "visible_fraction_of_causal": round(pairs / (w.seq_len * (w.seq_len + 1) / 2), 4),
+            "tflops": round(tflops(f_fwd + f_bwd, ms), 2), "ms_all_ranks": round(ms, 2),
+            "fwd_kernel_tflops": round(tflops(f_fwd, fwd_t.total_ms()), 2),
+            "bwd_kernel_tflops": round(tflops(f_bwd, bwd_t.total_ms()), 2)}
+
+
 def tflops(flops, ms):
     return flops / (ms * 1e-3) / 1e12
 
@@ -432,6 +470,7 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="skip the Pass Q / prefill / gathered legs")
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window layer leg")
     ap.add_argument("--no-large", action="store_true", help="skip the Llama-3-405B prefill leg")
+    ap.add_argument("--no-packed", action="store_true", help="skip the packed-document training leg")
     ap.add_argument("--window-workload", default="llama3_8b_window4k")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first make 3 device-to-device copies of this many MiB (counter calibration)")
@@ -507,6 +546,8 @@ def main():
         record["variants"] = measure_variants(torch, w, args.rank, max(1, args.steps // 2), 1)
     if not args.no_large:
         record["llama3_405b_fwd"] = measure_large(torch, inputs.WORKLOADS["llama3_405b_fwd"], args.rank, 1, 1)
+    if not args.no_packed:
+        record["llama3_8b_packed"] = measure_packed(torch, inputs.WORKLOADS["llama3_8b_packed"], 1, 1)
     if not args.no_window:
         record["sliding_window"] = measure_window(torch, inputs.WORKLOADS[args.window_workload], args.rank,
                                                   max(1, args.steps // 2), 1)

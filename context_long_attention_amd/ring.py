@@ -53,6 +53,7 @@ class RankRing:
         self.device = torch.device(device)
         self.pos = cpattn.cp_partition_zigzag(w.seq_len, w.cp, rank)
         self.packed = cu_seqlens is not None
+        self._live_pairs = {}
         if self.packed:
             self.cu_host = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
             self.cu_dev = torch.from_numpy(self.cu_host).to(self.device)
@@ -94,8 +95,18 @@ class RankRing:
         """Whether the local queries can see anything of ``src``'s block.  With a
         sliding window no longer than a chunk only the rank's own block and its
         ring neighbours' are live: the short exchange between neighbouring chips
-        of window layers ("Announcing Long-Context Training ...", closing section)."""
-        return any(m != cpattn.CP_MASK_SKIP for row in self.masks_of_source(src) for m in row)
+        of window layers ("Announcing Long-Context Training ...", closing section).
+        With packed documents the chunk classes cannot tell, so the visible pairs
+        are counted on the host (once per source): a block that only other
+        documents' queries could see is neither received nor computed."""
+        if not any(m != cpattn.CP_MASK_SKIP for row in self.masks_of_source(src) for m in row):
+            return False
+        if not self.packed:
+            return True
+        if src not in self._live_pairs:
+            step = (self.rank - src) % self.R
+            self._live_pairs[src] = cpattn.cp_count_pairs(self.problem(step, src, host_docs=True))
+        return self._live_pairs[src] > 0
 
     def step_pairs(self, step: int) -> int:
         """Visible (query, key) pairs per query head at ``step`` (host count)."""
