@@ -24,21 +24,34 @@ def _needs_gpu():
 @pytest.mark.timeout(900)
 def test_llama3_405b_forward_full_size_sampled():
     """Hq=128, Hkv=8 (G=16), D=128: rank 0's share of S=1M at CP=16 (local 64K), 16
-    ring steps of 64K-token KV blocks; final O/LSE on sampled rows and one step's
-    partial LSE."""
+    ring steps of 64K-token KV blocks.  The final O/LSE and every step's partial
+    (O_t, LSE_t), recomputed with the non-merging step kernel, on sampled rows (the
+    chunk edges and 32 uniform rows; each row costs the oracle about a second)."""
+    from context_long_attention_amd import cpattn
     from context_long_attention_amd.ring import RankRing
     w = inputs.WORKLOADS["llama3_405b_fwd"]
     note(f"fwd {w.name} full size rank 0")
     inp = RankInputs(w, 0)
     ring = RankRing(w, 0)
-    o, lse, steps = ring.forward(inp.q, inp.kv_of_source, keep_steps=False)
+    sched = ring.schedule()
+    o, lse, _ = ring.forward(inp.q, inp.kv_of_source, keep_steps=False)
     torch.cuda.synchronize()
-    rows = sampled_rows(w.local, w.chunk, 8, 3)
+    rows = sampled_rows(w.local, w.chunk, 32, 3)
     q_rows = widen(inp.q_bits[rows])
-    ro, rl, _ = oracle.rank_forward(q_rows, inp.qpos[rows], inp.blocks(ring.schedule()), None, w.scale)
+    ro, rl, rsteps = oracle.rank_forward(q_rows, inp.qpos[rows], inp.blocks(sched), None, w.scale)
     assert_o_close(o[rows].cpu().numpy(), ro, "405B O sampled rows")
     assert_lse_close(lse[:, rows].cpu().numpy(), rl, "405B LSE sampled rows")
     assert not torch.isnan(o).any().item()
+    rows_dev = torch.from_numpy(rows).cuda()
+    o_t = torch.empty_like(o)
+    l_t = torch.empty_like(lse)
+    for t, (rot, rlt) in enumerate(rsteps):
+        k, v = inp.kv_of_source(sched[t])
+        cpattn.cp_attn_fwd_step(ring.problem(t), inp.q, k, v, o_t, l_t)
+        got_o = o_t.index_select(0, rows_dev).cpu().numpy()
+        got_l = l_t.index_select(1, rows_dev).cpu().numpy()
+        assert_lse_close(got_l, rlt, f"405B LSE_t step {t}")
+        assert_o_close(got_o, rot, f"405B O_t step {t}", np.isfinite(rlt).T)
 
 
 def _packed_setup():
