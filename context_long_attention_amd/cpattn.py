@@ -24,7 +24,7 @@ CP_TILE_SKIP, CP_TILE_PARTIAL, CP_TILE_FULL = 0, 1, 2
 EXPORTS = (
     "cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition_zigzag", "cp_ring_source",
     "cp_step_masks", "cp_step_masks_window", "cp_tile_shape", "cp_block_map_size", "cp_block_map", "cp_count_pairs",
-    "cp_attn_fwd_step", "cp_merge_partials", "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step",
+    "cp_bwd_kv_split", "cp_attn_fwd_step", "cp_merge_partials", "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step",
     "cp_debug_clock_probe",
 )
 
@@ -49,6 +49,7 @@ class cp_attn_problem(ctypes.Structure):
         ("mask", (ctypes.c_int32 * 2) * 2),
         ("cu_seqlens", ctypes.c_void_p), ("n_docs", ctypes.c_int32),
         ("window", ctypes.c_int32),
+        ("kv_split", ctypes.c_int32),
     ]
 
 
@@ -77,6 +78,7 @@ def lib():
             "cp_block_map_size": ([P, vp, vp], i32),
             "cp_block_map": ([P, vp], i32),
             "cp_count_pairs": ([P, vp], i32),
+            "cp_bwd_kv_split": ([P, i32, vp], i32),
             "cp_attn_fwd_step": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
             "cp_merge_partials": ([f32p, f32p, f32p, f32p, i64, i32, i32, vp], i32),
             "cp_attn_fwd_step_merge": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
@@ -152,9 +154,10 @@ def cp_tile_shape(hq: int, hkv: int, head_dim: int) -> tuple[int, int]:
 
 
 def make_problem(hq, hkv, head_dim, scale, q_rows, kv_rows, q_segments, kv_segments, masks,
-                 cu_seqlens_ptr=None, n_docs=0, window=0) -> cp_attn_problem:
+                 cu_seqlens_ptr=None, n_docs=0, window=0, kv_split=0) -> cp_attn_problem:
     """Fill a cp_attn_problem.  Segments are (row0, pos0, len) triples; window is
-    the sliding window in tokens (0: none)."""
+    the sliding window in tokens (0: none); kv_split the backward's dK/dV work
+    split (0: chosen by the library)."""
     p = cp_attn_problem()
     p.hq, p.hkv, p.head_dim, p.scale = hq, hkv, head_dim, scale
     p.q_rows, p.kv_rows = q_rows, kv_rows
@@ -169,6 +172,7 @@ def make_problem(hq, hkv, head_dim, scale, q_rows, kv_rows, q_segments, kv_segme
     p.cu_seqlens = cu_seqlens_ptr
     p.n_docs = n_docs
     p.window = window
+    p.kv_split = kv_split
     return p
 
 
@@ -184,6 +188,13 @@ def cp_block_map(p: cp_attn_problem) -> np.ndarray:
     out = np.zeros((nq, nk), dtype=np.uint8)
     _check(lib().cp_block_map(ctypes.byref(p), out.ctypes.data_as(ctypes.c_void_p)))
     return out
+
+
+def cp_bwd_kv_split(p: cp_attn_problem, n_cu: int) -> int:
+    """dK/dV work split for p (HOST cu_seqlens) on a GPU with n_cu CUs."""
+    out = ctypes.c_int32()
+    _check(lib().cp_bwd_kv_split(ctypes.byref(p), n_cu, ctypes.byref(out)))
+    return out.value
 
 
 def cp_count_pairs(p: cp_attn_problem) -> int:

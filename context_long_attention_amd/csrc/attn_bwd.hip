@@ -26,6 +26,7 @@
 // exchange for no atomic traffic and two clean streaming loops.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -60,8 +61,8 @@ struct BwdParams {
     int32_t qs_row0[2], qs_pos0[2], qs_len[2];
     int32_t ks_row0[2], ks_pos0[2], ks_len[2];
     int32_t mask[2][2];
-    // dK/dV kernel: 128-key tiles
-    int32_t ktiles0, n_ktiles, n_work_kv;
+    // dK/dV kernel: 128-key tiles, each spread over kv_split workgroups
+    int32_t ktiles0, n_ktiles, n_work_kv, kv_split;
     // dQ kernel: query tiles of BMQ rows
     int32_t qtiles0, n_qtiles, n_work_q, n_hb;
 };
@@ -99,12 +100,15 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     const int hl = lane >> 5;
     const int ql = lane & 31;
 
-    // item w runs on XCD w mod 8 (workgroups are dealt round-robin): KV head
-    // w mod Hkv, key tiles earliest first (the most queries)
+    // workgroup w takes part w / n_work_kv of key block b = w mod n_work_kv, which
+    // runs on XCD b mod 8 when n_work_kv is a multiple of 8 (workgroups are dealt
+    // round-robin): KV head b mod Hkv, key tiles earliest first (the most queries)
     const int w = blockIdx.x;
-    if (w >= p.n_work_kv) return;
-    const int g = w % p.hkv;
-    const int kt = w / p.hkv;
+    if (w >= p.n_work_kv * p.kv_split) return;
+    const int part = w / p.n_work_kv;
+    const int b = w - part * p.n_work_kv;
+    const int g = b % p.hkv;
+    const int kt = b / p.hkv;
     const int s = (kt < p.ktiles0) ? 0 : 1;
     const int kt_in = s ? kt - p.ktiles0 : kt;
     const int key_row0 = p.ks_row0[s] + kt_in * BK;
@@ -189,15 +193,19 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     }
     const int n0 = thi[0] - tlo[0];
     const int per_head = n0 + (thi[1] - tlo[1]);
-    const int n_it = per_head * p.group;
+    const int n_all = per_head * p.group;
+    // this workgroup's part of the block's items: [it0, it0 + n_it)
+    const int it0 = (int)((int64_t)n_all * part / p.kv_split);
+    const int n_it = (int)((int64_t)n_all * (part + 1) / p.kv_split) - it0;
     const int qrow_bytes = p.hq * D * 2;
 
     struct Item {
         int head, qs, tq;
     };
     auto item_of = [&](int it) -> Item {
-        const int head = g * p.group + it / max(per_head, 1);
-        const int rem = it - (head - g * p.group) * per_head;
+        const int gi = it0 + it;
+        const int head = g * p.group + gi / max(per_head, 1);
+        const int rem = gi - (head - g * p.group) * per_head;
         const int qs = (rem < n0) ? 0 : 1;
         return Item{head, qs, qs ? tlo[1] + (rem - n0) : tlo[0] + rem};
     };
@@ -328,8 +336,50 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
         }
     }
 
-    // ---- write this workgroup's dK (scaled) and dV rows
-    if (key_valid) {
+    // ---- write this workgroup's dK (scaled) and dV rows, or with a split add
+    // them to the cleared outputs.  The adds go through LDS so that each atomic
+    // instruction covers 64 consecutive floats of one row rather than one float
+    // of 32 rows: every wave stages its 32 rows, half of the dims in its query
+    // slot and half in its dO slot (free once the ring has drained), as rows of
+    // D/2 floats with 16-byte chunks XOR-swizzled by row.
+    if (p.kv_split > 1) {
+        constexpr int HALF = D / 2, NCH = HALF / 4, ROWB = HALF * 4;
+        static_assert(32 * ROWB <= L::BYTES, "a ring slot holds half of a wave's rows");
+        __syncthreads();  // every wave is done with the ring
+        if (n_it > 0) {
+            char* st[2] = {pick(wave == 0, qt0, pick(wave == 1, qt1, pick(wave == 2, qt2, qt3))),
+                           pick(wave == 0, ot0, pick(wave == 1, ot1, pick(wave == 2, ot2, ot3)))};
+            const int64_t row0 = (int64_t)(key_row0 + 32 * wave) * kv_stride + (int64_t)g * D;
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const f32x16* acc = t ? dva : dka;
+                const float mul = t ? 1.f : p.scale;
+#pragma unroll
+                for (int db = 0; db < DB; ++db)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int d = 32 * db + 8 * i + 4 * hl;
+                        const int ch = (d % HALF) / 4;
+                        const f32x4 x = {acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul, acc[db][4 * i + 2] * mul,
+                                         acc[db][4 * i + 3] * mul};
+                        *reinterpret_cast<f32x4*>(st[d / HALF] + ql * ROWB + ((ch ^ (ql % NCH)) * 16)) = x;
+                    }
+                __syncthreads();
+                float* out = t ? p.dv : p.dk;
+                constexpr int RPI = 64 / HALF;  // rows per instruction (1 at D = 128, 2 at D = 64)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll 4
+                    for (int r0 = 0; r0 < 32; r0 += RPI) {
+                        const int r = r0 + lane / HALF, dl = lane % HALF;
+                        const float x = *reinterpret_cast<const float*>(st[h] + r * ROWB +
+                                                                        (((dl / 4) ^ (r % NCH)) * 16) + 4 * (dl % 4));
+                        if (32 * wave + r < kcount) unsafeAtomicAdd(out + row0 + (int64_t)r * kv_stride + h * HALF + dl, x);
+                    }
+                __syncthreads();
+            }
+        }
+    } else if (key_valid) {
         const int64_t base = (int64_t)(key_row0 + kk) * kv_stride + (int64_t)g * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
@@ -601,6 +651,29 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
     }
 }
 
+// Clear rows [r0, r0 + n0) and [r1, r1 + n1) (in units of `row` floats, a
+// multiple of 4) of a and b: the dK/dV rows that split workgroups add into.
+__global__ __launch_bounds__(256) void clear_rows_kernel(float* a, float* b, int64_t r0, int64_t n0, int64_t r1,
+                                                         int64_t n1, int64_t row) {
+    const int64_t n4 = (n0 + n1) * row / 4;
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t f = 4 * i;  // float index within the two runs
+        const int64_t at = (f < n0 * row) ? r0 * row + f : r1 * row + (f - n0 * row);
+        *reinterpret_cast<f32x4*>(a + at) = z;
+        *reinterpret_cast<f32x4*>(b + at) = z;
+    }
+}
+
+// CUs of the current device (2 dK/dV workgroups run on each); 256 if unknown.
+int64_t device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+        return 256;
+    return n;
+}
+
 template <int D>
 hipError_t launch_dkdv(const BwdParams& prm, int grid, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<D>), dim3(grid), dim3(kKvThreads), 0, stream, prm);
@@ -675,9 +748,23 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     prm.n_work_kv = int32_t(work_kv);
     prm.n_work_q = int32_t(work_q);
     prm.n_hb = p->hq / gq.hpw;
+    prm.kv_split = (p->kv_split > 0) ? p->kv_split : dkdv_split(p, nullptr, device_cus());
     hipError_t e = hipSuccess;
+    if (work_kv > 0 && prm.kv_split > 1) {
+        // split workgroups add into dK/dV: clear the rows of both KV segments first
+        const int64_t row = int64_t(p->hkv) * p->head_dim;
+        const int64_t n0 = prm.ks_len[0], n1 = prm.ks_len[1];
+        const int64_t n4 = (n0 + n1) * row / 4;
+        const int blocks = int(std::min<int64_t>(ceil_div(n4, 256), 4096));
+        hipLaunchKernelGGL(clear_rows_kernel, dim3(blocks), dim3(256), 0, stream, dk_out, dv_out,
+                           int64_t(prm.ks_row0[0]), n0, int64_t(prm.ks_row0[1]), n1, row);
+        e = hipGetLastError();
+        if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("dK/dV clear launch: ") + hipGetErrorString(e));
+    }
     if (work_kv > 0) {
-        const int grid = int(work_kv);
+        if (work_kv * prm.kv_split > (int64_t(1) << 30))
+            return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
+        const int grid = int(work_kv * prm.kv_split);
         e = (p->head_dim == 128) ? launch_dkdv<128>(prm, grid, stream) : launch_dkdv<64>(prm, grid, stream);
         if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd dK/dV launch: ") + hipGetErrorString(e));
     }

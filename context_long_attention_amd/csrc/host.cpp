@@ -54,6 +54,8 @@ cp_status validate_problem(const cp_attn_problem* p, bool device_docs) {
     if (p->n_q_seg < 1 || p->n_q_seg > 2 || p->n_kv_seg < 1 || p->n_kv_seg > 2)
         return fail(CP_ERR_INVALID_ARG, "segment counts must be 1 or 2");
     if (p->window < 0) return fail(CP_ERR_INVALID_ARG, "window must be >= 0");
+    if (p->kv_split < 0 || p->kv_split > kMaxKvSplit)
+        return fail(CP_ERR_INVALID_ARG, "kv_split must be in [0, " + std::to_string(kMaxKvSplit) + "]");
     bool any_doc = false;
     for (int i = 0; i < p->n_q_seg; ++i) {
         const cp_segment& s = p->q_seg[i];
@@ -103,6 +105,66 @@ int64_t row_lower_bound(const cp_attn_problem* p, int mask, int64_t q) {
     if (mask == CP_MASK_DOC) lo = doc_start_host(p->cu_seqlens, p->n_docs, q);
     if (p->window > 0 && (mask == CP_MASK_DOC || mask == CP_MASK_DIAG_CAUSAL)) lo = std::max(lo, q - p->window + 1);
     return lo;
+}
+
+int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_cu) {
+    // Per 128-key block: the query tiles (of kBwdQRows rows, per query head) that
+    // see one of its keys, by the ranges the dK/dV kernel walks.  With documents
+    // and no host cu_seqlens the ranges are unknown: no split.
+    bool any_doc = false;
+    for (int i = 0; i < p->n_q_seg; ++i)
+        for (int j = 0; j < p->n_kv_seg; ++j) any_doc |= (p->mask[i][j] == CP_MASK_DOC);
+    if (any_doc && !host_cu) return 1;
+    constexpr int64_t kInf = std::numeric_limits<int64_t>::max();
+    const int64_t group = p->hq / p->hkv;
+    int64_t total = 0, most = 0;
+    for (int j = 0; j < p->n_kv_seg; ++j) {
+        const cp_segment& ks = p->kv_seg[j];
+        for (int64_t kb = 0; kb < ceil_div(ks.len, kBwdKeysPerWG); ++kb) {
+            const int64_t k0 = ks.pos0 + kb * kBwdKeysPerWG;
+            const int64_t k1 = std::min(ks.pos0 + ks.len, k0 + kBwdKeysPerWG) - 1;
+            int64_t items = 0;
+            for (int i = 0; i < p->n_q_seg; ++i) {
+                const cp_segment& qs = p->q_seg[i];
+                const int m = p->mask[i][j];
+                const int64_t nqt = ceil_div(qs.len, kBwdQRows);
+                if (m == CP_MASK_SKIP || qs.len == 0) continue;
+                if (m == CP_MASK_FULL) {
+                    items += nqt;
+                    continue;
+                }
+                if (k0 > qs.pos0 + qs.len - 1) continue;  // causal: rows q >= k0
+                const int64_t lo = (k0 <= qs.pos0) ? 0 : (k0 - qs.pos0) / kBwdQRows;
+                // rows q < end of the last key's document and q < k1 + window
+                int64_t qe = kInf;
+                if (m == CP_MASK_DOC) {
+                    int32_t a = 0, b = p->n_docs - 1;  // last document starting at or before k1
+                    while (a < b) {
+                        const int32_t mid = (a + b + 1) / 2;
+                        if (host_cu[mid] <= k1)
+                            a = mid;
+                        else
+                            b = mid - 1;
+                    }
+                    qe = host_cu[a + 1];
+                }
+                if (p->window > 0) qe = std::min(qe, k1 + p->window);
+                int64_t hi = nqt;
+                if (qe != kInf) hi = (qe - 1 < qs.pos0) ? 0 : std::min(nqt, (qe - 1 - qs.pos0) / kBwdQRows + 1);
+                items += std::max<int64_t>(0, hi - lo);
+            }
+            items *= group;
+            total += items * p->hkv;
+            most = std::max(most, items);
+        }
+    }
+    // Two dK/dV workgroups run per CU.  Split when the largest block holds more
+    // than twice the items of an even share of those slots (and than a floor
+    // that keeps a split workgroup's fixed costs small).
+    const int64_t slots = 2 * std::max<int64_t>(1, n_cu);
+    const int64_t share = std::max<int64_t>(ceil_div(total, slots), kMinSplitItems);
+    if (most <= 2 * share) return 1;
+    return int32_t(std::min<int64_t>(kMaxKvSplit, ceil_div(most, share)));
 }
 
 TileRange tile_range(int mask, int64_t q0, int64_t q1, int64_t lo0, int64_t kpos0, int64_t klen, int bn) {
@@ -279,6 +341,15 @@ cp_status cp_block_map(const cp_attn_problem* p, uint8_t* map_out) {
             }
         }
     }
+    return CP_OK;
+}
+
+cp_status cp_bwd_kv_split(const cp_attn_problem* p, int32_t n_cu, int32_t* split_out) {
+    if (!split_out) return fail(CP_ERR_INVALID_ARG, "split_out is NULL");
+    if (n_cu < 1) return fail(CP_ERR_INVALID_ARG, "n_cu must be positive");
+    cp_status st = validate_problem(p, false);
+    if (st != CP_OK) return st;
+    *split_out = dkdv_split(p, p->cu_seqlens, n_cu);
     return CP_OK;
 }
 

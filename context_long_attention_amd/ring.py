@@ -54,6 +54,7 @@ class RankRing:
         self.pos = cpattn.cp_partition_zigzag(w.seq_len, w.cp, rank)
         self.packed = cu_seqlens is not None
         self._live_pairs = {}
+        self._kv_split = {}
         if self.packed:
             self.cu_host = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
             self.cu_dev = torch.from_numpy(self.cu_host).to(self.device)
@@ -107,6 +108,18 @@ class RankRing:
             step = (self.rank - src) % self.R
             self._live_pairs[src] = cpattn.cp_count_pairs(self.problem(step, src, host_docs=True))
         return self._live_pairs[src] > 0
+
+    def kv_split(self, src: int) -> int:
+        """dK/dV work split of the backward step on ``src``'s block.  With packed
+        documents the library cannot see the (device) document table, so the
+        split comes from the host copy; otherwise the library chooses (0)."""
+        if not self.packed:
+            return 0
+        if src not in self._kv_split:
+            step = (self.rank - src) % self.R
+            n_cu = torch.cuda.get_device_properties(self.device).multi_processor_count
+            self._kv_split[src] = cpattn.cp_bwd_kv_split(self.problem(step, src, host_docs=True), n_cu)
+        return self._kv_split[src]
 
     def step_pairs(self, step: int) -> int:
         """Visible (query, key) pairs per query head at ``step`` (host count)."""
@@ -201,6 +214,7 @@ class RankRing:
                 dk = torch.empty((rows, w.hkv, w.dim), dtype=torch.float32, device=dev)
                 dv = torch.empty_like(dk)
             p = self.problem(t, src)
+            p.kv_split = self.kv_split(src)
             if timer:
                 timer(t, "bwd_begin", compute)
             cpattn.cp_attn_bwd_step(p, q, k, v, d_o, lse, delta, dq, dk, dv, stream=compute)

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 3
+#define CPATTN_ABI_VERSION 4
 
 typedef enum cp_status {
     CP_OK = 0,
@@ -102,6 +102,13 @@ typedef struct cp_attn_problem {
     const int32_t* cu_seqlens;
     int32_t n_docs;
     int32_t window;           /* sliding window in tokens, 0 = none (>= 0) */
+    /* Backward only: the number of workgroups (1..8) over which the dK/dV
+     * kernel spreads each 128-key block's query tiles; 0 = chosen by the
+     * library from the positions (1 when a mask is DOC, whose ranges need the
+     * documents on the host: see cp_bwd_kv_split).  Above 1, dK/dV are
+     * cleared and then summed in fp32 with atomic adds, so their last bits may
+     * vary between runs.  The forward calls ignore it. */
+    int32_t kv_split;
 } cp_attn_problem;
 
 /* ---------------------------------------------------------------- host ---- */
@@ -240,6 +247,15 @@ cp_status cp_attn_bwd_prep(const void* d_o, const float* o, float* delta, int64_
  *   dk_out, dv_out device fp32 [kv_rows, Hkv, D]  OVERWRITTEN: this step's
  *            contribution of the local queries to the visiting block; rows
  *            outside every KV segment are not written. */
+/* Split of the dK/dV work that cp_attn_bwd_step would choose for kv_split = 0,
+ * computed here with HOST cu_seqlens, so DOC problems can be balanced too: a
+ * key block that many more query tiles see than an even share of the GPU's
+ * dK/dV slots (2 per CU, n_cu CUs) is spread over up to 8 workgroups.  Such
+ * blocks occur where visibility is a band or a triangle (sliding windows, the
+ * edge of a document).  Writes 1..8 to split_out.  INVALID_ARG on a bad
+ * problem, n_cu < 1 or a NULL split_out. */
+cp_status cp_bwd_kv_split(const cp_attn_problem* p, int32_t n_cu, int32_t* split_out);
+
 cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v,
                            const void* d_o, const float* lse, const float* delta, float* dq_acc,
                            float* dk_out, float* dv_out, hipStream_t stream);

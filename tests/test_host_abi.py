@@ -272,3 +272,39 @@ def test_ring_masks_follow_the_block_not_the_step():
             p = ring.problem(t, src, host_docs=True)
             assert [[p.mask[i][j] for j in range(2)] for i in range(2)] == \
                 cpattn.cp_step_masks_window(64, 4, 1, natural, False, 12)
+
+
+def test_kv_split_rule():
+    """The dK/dV work split: 1 on balanced causal steps, > 1 where a sliding window
+    leaves a triangle of pairs (a few key blocks see most of the queries), within
+    [1, 8] everywhere, and never smaller on a GPU with more CUs."""
+    w = inputs.WORKLOADS["llama3_8b_fwdbwd"]
+    ring = RankRing(w, 0, device="cpu")
+    for t in range(w.cp):
+        assert cpattn.cp_bwd_kv_split(ring.problem(t, host_docs=True), 256) == 1
+    ww = inputs.WORKLOADS["llama3_8b_window4k"]
+    ring = RankRing(ww, 0, device="cpu")
+    assert cpattn.cp_bwd_kv_split(ring.problem(0, host_docs=True), 256) == 1
+    p7 = ring.problem(ww.cp - 1, host_docs=True)  # the neighbour block: a 4K-wide triangle
+    assert cpattn.cp_bwd_kv_split(p7, 256) >= 2
+    splits = [cpattn.cp_bwd_kv_split(p7, n) for n in (8, 32, 128, 256, 1024, 4096)]
+    assert splits == sorted(splits) and 1 <= splits[0] and splits[-1] <= 8
+    wp = inputs.WORKLOADS["llama3_8b_packed"]
+    ring = RankRing(wp, 5, wp.cu_seqlens(), device="cpu")
+    for t in range(wp.cp):
+        assert 1 <= cpattn.cp_bwd_kv_split(ring.problem(t, host_docs=True), 256) <= 8
+
+
+def test_kv_split_validation():
+    F = cpattn.CP_MASK_FULL
+    p = cpattn.make_problem(4, 2, 128, 0.1, 64, 64, [(0, 0, 64)], [(0, 0, 64)], [[F, F], [F, F]])
+    with pytest.raises(cpattn.CpError) as e:
+        cpattn.cp_bwd_kv_split(p, 0)
+    assert e.value.status == cpattn.CP_ERR_INVALID_ARG
+    for bad in (-1, 9):
+        p.kv_split = bad
+        with pytest.raises(cpattn.CpError) as e:
+            cpattn.cp_count_pairs(p)
+        assert e.value.status == cpattn.CP_ERR_INVALID_ARG
+    p.kv_split = 8
+    assert cpattn.cp_count_pairs(p) == 64 * 64
