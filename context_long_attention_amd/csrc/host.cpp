@@ -5,7 +5,9 @@
 #include <cmath>
 #include <cstring>
 #include <limits>
+#include <queue>
 #include <string>
+#include <vector>
 
 #include "internal.h"
 
@@ -117,20 +119,20 @@ int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_c
     if (any_doc && !host_cu) return 1;
     constexpr int64_t kInf = std::numeric_limits<int64_t>::max();
     const int64_t group = p->hq / p->hkv;
-    int64_t total = 0, most = 0;
+    std::vector<int64_t> items;  // per block, in the kernel's key-tile order
     for (int j = 0; j < p->n_kv_seg; ++j) {
         const cp_segment& ks = p->kv_seg[j];
         for (int64_t kb = 0; kb < ceil_div(ks.len, kBwdKeysPerWG); ++kb) {
             const int64_t k0 = ks.pos0 + kb * kBwdKeysPerWG;
             const int64_t k1 = std::min(ks.pos0 + ks.len, k0 + kBwdKeysPerWG) - 1;
-            int64_t items = 0;
+            int64_t n = 0;
             for (int i = 0; i < p->n_q_seg; ++i) {
                 const cp_segment& qs = p->q_seg[i];
                 const int m = p->mask[i][j];
                 const int64_t nqt = ceil_div(qs.len, kBwdQRows);
                 if (m == CP_MASK_SKIP || qs.len == 0) continue;
                 if (m == CP_MASK_FULL) {
-                    items += nqt;
+                    n += nqt;
                     continue;
                 }
                 if (k0 > qs.pos0 + qs.len - 1) continue;  // causal: rows q >= k0
@@ -151,20 +153,52 @@ int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_c
                 if (p->window > 0) qe = std::min(qe, k1 + p->window);
                 int64_t hi = nqt;
                 if (qe != kInf) hi = (qe - 1 < qs.pos0) ? 0 : std::min(nqt, (qe - 1 - qs.pos0) / kBwdQRows + 1);
-                items += std::max<int64_t>(0, hi - lo);
+                n += std::max<int64_t>(0, hi - lo);
             }
-            items *= group;
-            total += items * p->hkv;
-            most = std::max(most, items);
+            items.push_back(n * group);
         }
     }
-    // Two dK/dV workgroups run per CU.  Split when the largest block holds more
-    // than twice the items of an even share of those slots (and than a floor
-    // that keeps a split workgroup's fixed costs small).
+    // Makespan of the launch in item times when workgroup w starts on the first
+    // free slot in id order (two dK/dV workgroups per CU): part w / n_blocks of
+    // block w mod n_blocks, whose key blocks run KV-head-minor.  A workgroup also
+    // costs a fixed overhead (its K/V rows, the ring's fill and drain, the output
+    // writes: about kWgOverhead items, one more with a split) and an empty one
+    // half an item.
     const int64_t slots = 2 * std::max<int64_t>(1, n_cu);
-    const int64_t share = std::max<int64_t>(ceil_div(total, slots), kMinSplitItems);
-    if (most <= 2 * share) return 1;
-    return int32_t(std::min<int64_t>(kMaxKvSplit, ceil_div(most, share)));
+    const int64_t n_blocks = int64_t(items.size()) * p->hkv;
+    if (n_blocks == 0 || n_blocks * kMaxKvSplit > (int64_t(1) << 22)) return 1;
+    auto makespan = [&](int64_t split) {
+        std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
+        double end = 0.0;
+        for (int64_t w = 0; w < split * n_blocks; ++w) {
+            const int64_t part = w / n_blocks, kt = (w % n_blocks) / p->hkv;
+            const int64_t n = items[kt];
+            const int64_t mine = n * (part + 1) / split - n * part / split;
+            const double cost = mine ? double(mine) + kWgOverhead + (split > 1 ? 1.0 : 0.0) : 0.5;
+            double start = 0.0;
+            if (int64_t(free_at.size()) == slots) {
+                start = free_at.top();
+                free_at.pop();
+            }
+            free_at.push(start + cost);
+            end = std::max(end, start + cost);
+        }
+        return end;
+    };
+    // No split can beat the even share of all items over the slots: stop if the
+    // launch without one is within 3% of it.  Otherwise take the smallest of 2, 4
+    // and 8 within 3% of the best, if that gains 3% over no split.
+    const double one = makespan(1);
+    double total = 0.0;
+    for (int64_t n : items) total += double(n) * p->hkv;
+    if (one <= 1.03 * (total / double(slots))) return 1;
+    const int64_t cand[3] = {2, 4, kMaxKvSplit};
+    double t[3], best = one;
+    for (int c = 0; c < 3; ++c) best = std::min(best, t[c] = makespan(cand[c]));
+    if (best > 0.97 * one) return 1;
+    for (int c = 0; c < 3; ++c)
+        if (t[c] <= 1.03 * best) return int32_t(cand[c]);
+    return 1;
 }
 
 TileRange tile_range(int mask, int64_t q0, int64_t q1, int64_t lo0, int64_t kpos0, int64_t klen, int bn) {

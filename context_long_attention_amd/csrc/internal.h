@@ -26,10 +26,10 @@ TileGeom fwd_geom(int hq, int hkv);
 constexpr int kBwdKeysPerWG = 128;
 constexpr int kBwdQRows = 32;
 // A key block's query items may be spread over up to kMaxKvSplit workgroups,
-// each adding its part of dK/dV; a split workgroup gets at least about
-// kMinSplitItems items.
+// each adding its part of dK/dV.  kWgOverhead: the fixed cost of a dK/dV
+// workgroup in item times (used to choose the split).
 constexpr int kMaxKvSplit = 8;
-constexpr int64_t kMinSplitItems = 16;
+constexpr double kWgOverhead = 3.0;
 
 void set_error(const std::string& msg);
 cp_status fail(cp_status s, const std::string& msg);
@@ -72,9 +72,9 @@ int64_t doc_start_host(const int32_t* cu, int32_t n_docs, int64_t pos);
 int64_t row_lower_bound(const cp_attn_problem* p, int mask, int64_t q);
 
 // Number of workgroups (1..kMaxKvSplit) over which the dK/dV kernel spreads
-// each key block's query items, from the items of every block (the ranges that
-// kernel walks) and the CU count.  host_cu: host cu_seqlens for DOC masks;
-// NULL with a DOC mask gives 1.
+// each key block's query items: the one with the shortest simulated launch,
+// from the items of every block (the ranges that kernel walks) and the CU
+// count.  host_cu: host cu_seqlens for DOC masks; NULL with a DOC mask gives 1.
 int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_cu);
 
 }  // namespace cpattn
