@@ -743,6 +743,8 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     if (work_kv == 0 && work_q == 0) return CP_OK;
     if (!q || !k || !v || !d_o || !lse || !delta || !dq_acc || !dk_out || !dv_out)
         return fail(CP_ERR_INVALID_ARG, "NULL tensor pointer");
+    if (!all_aligned16({q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out}))
+        return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
     if (work_kv > (int64_t(1) << 30) || work_q > (int64_t(1) << 30))
         return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     prm.n_work_kv = int32_t(work_kv);

@@ -648,6 +648,7 @@ cp_status fwd_step(const cp_attn_problem* p, const void* q, const void* k, const
     if (n_work == 0) return CP_OK;
     if (!q || !o_step || !lse_step) return fail(CP_ERR_INVALID_ARG, "NULL tensor pointer");
     if (nk > 0 && (!k || !v)) return fail(CP_ERR_INVALID_ARG, "NULL K/V pointer");
+    if (!all_aligned16({q, k, v, o_step, lse_step})) return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
     if (n_work > (int64_t(1) << 30)) return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     if (!kv_spans_fit(p)) return fail(CP_ERR_UNSUPPORTED, "a KV segment spans 1 GiB or more");
     prm.n_work = int32_t(n_work);

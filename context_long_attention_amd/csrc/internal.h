@@ -3,6 +3,7 @@
 #pragma once
 
 #include <cstdint>
+#include <initializer_list>
 #include <string>
 
 #include "cpattn.h"
@@ -40,6 +41,14 @@ cp_status fail(cp_status s, const std::string& msg);
 cp_status validate_problem(const cp_attn_problem* p, bool device_docs);
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The kernels move every tensor in 16-byte vectors: each tensor pointer must be
+// 16-byte aligned (a torch allocation, or a view of it starting at a row, is).
+inline bool all_aligned16(std::initializer_list<const void*> ptrs) {
+    for (const void* q : ptrs)
+        if (reinterpret_cast<uintptr_t>(q) & 15u) return false;
+    return true;
+}
 
 // The step kernels address a KV tile by a 32-bit byte offset into a buffer
 // descriptor spanning one segment of one KV head, so every KV segment must

@@ -93,6 +93,8 @@ extern "C" cp_status cp_merge_partials(float* o_acc, float* lse_acc, const float
     if (head_dim != 64 && head_dim != 128) return fail(CP_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (rows == 0) return CP_OK;
     if (!o_acc || !lse_acc || !o_step || !lse_step) return fail(CP_ERR_INVALID_ARG, "NULL pointer");
+    if (!all_aligned16({o_acc, lse_acc, o_step, lse_step}))
+        return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
     const int64_t threads = rows * heads * (head_dim / 4);
     const int64_t grid = ceil_div(threads, kThreads);
     if (grid > 0x7fffffff) return fail(CP_ERR_UNSUPPORTED, "too large");
@@ -113,6 +115,7 @@ extern "C" cp_status cp_attn_bwd_prep(const void* d_o, const float* o, float* de
     if (head_dim != 64 && head_dim != 128) return fail(CP_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (rows == 0) return CP_OK;
     if (!d_o || !o || !delta) return fail(CP_ERR_INVALID_ARG, "NULL pointer");
+    if (!all_aligned16({d_o, o, delta})) return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
     const int64_t threads = rows * heads * (head_dim / 4);
     const int64_t grid = ceil_div(threads, kThreads);
     if (grid > 0x7fffffff) return fail(CP_ERR_UNSUPPORTED, "too large");

@@ -176,6 +176,11 @@ cp_status cp_count_pairs(const cp_attn_problem* p, int64_t* pairs_out);
 
 /* -------------------------------------------------------------- device ---- */
 
+/* Device calls: every tensor pointer is a device address, 16-byte aligned (the
+ * kernels move 16-byte vectors; a torch allocation, or a view of it starting
+ * at a row, qualifies).  A misaligned or NULL tensor gives INVALID_ARG before
+ * anything is launched.  Launches are asynchronous on `stream`. */
+
 /* Forward of one ring step: blockwise flash attention of the local queries
  * against the KV block held at this step ("Announcing Long-Context Training
  * ...", section "Built on a fast attention kernel": the kernel runs once per

@@ -143,6 +143,20 @@ def test_validation_rejects_bad_problems(lib):
     assert lib.cp_merge_partials(None, None, None, None, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
     assert lib.cp_attn_bwd_prep(None, None, None, 10, 4, 72, None) == cpattn.CP_ERR_UNSUPPORTED
     assert b"head_dim" in lib.cp_last_error()
+    # misaligned tensor pointers are rejected before any launch (never dereferenced;
+    # checked only without a GPU, where a regression could not launch on them)
+    import torch
+    if torch.cuda.is_available():
+        return
+    p = cpattn.make_problem(**good)
+    ok, bad = 1 << 20, (1 << 20) + 8
+    assert lib.cp_attn_fwd_step(ctypes.byref(p), bad, ok, ok, ok, ok, None, None) == cpattn.CP_ERR_INVALID_ARG
+    assert b"aligned" in lib.cp_last_error()
+    assert lib.cp_attn_fwd_step_merge(ctypes.byref(p), ok, ok, ok, ok, bad, None, None) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_attn_bwd_step(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, ok, bad,
+                                None) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_merge_partials(ok, ok, bad, ok, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_attn_bwd_prep(ok, ok, bad, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
 
 
 def test_clock_probe_arguments(lib):
