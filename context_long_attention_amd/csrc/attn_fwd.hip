@@ -109,9 +109,9 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     const int ql = lane & 31;
 
     // ---- work decode.  Workgroups are dealt to the 8 XCDs round-robin by id, so
-    // item w goes to XCD w mod 8: head block w mod n_hb (every XCD keeps the same
-    // head blocks, whose K/V then stay in its L2) and query tiles latest first
-    // (the most keys), interleaved across the XCDs sharing a head block.
+    // item w goes to XCD w mod 8: head block u = w mod n_hb (every XCD keeps the
+    // same head blocks, whose K/V then stay in its L2) and query tiles latest
+    // first (the most keys), interleaved across the XCDs sharing a head block.
     const int w = blockIdx.x;
     if (w >= p.n_work) return;
     const bool probe = p.clk != nullptr && w < p.clk_wgs;
@@ -120,7 +120,16 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         t0_cycles = __builtin_readcyclecounter();
         t0_ticks = __builtin_readsteadycounter();
     }
-    const int hb = w % p.n_hb;
+    // With Hkv a multiple of 8 the head blocks of a KV head all go to one XCD
+    // (u mod 8 picks the KV head), so each XCD streams the K/V of Hkv / 8 KV
+    // heads rather than of several per round; the map is the identity when a
+    // KV head has one head block.
+    const int u = w % p.n_hb;
+    int hb = u;
+    if ((p.hkv & 7) == 0) {
+        const int nb = p.n_hb / p.hkv;  // head blocks per KV head
+        hb = ((u & 7) + 8 * ((u >> 3) / nb)) * nb + (u >> 3) % nb;
+    }
     const int qt = p.n_qtiles - 1 - w / p.n_hb;
     const int qs = (qt < p.qtiles0) ? 0 : 1;
     const int qt_in = qs ? qt - p.qtiles0 : qt;

@@ -105,9 +105,10 @@ def stats_markdown(path: str, commands, top: int = 12, title: str | None = None)
 
 
 def counters_by_dispatch(path: str, counter: str):
-    """kernel short name -> list of (dispatch id, value summed over the counter's instances)."""
+    """kernel short name -> list of (dispatch id, value summed over the counter's
+    instances, grid size in work-items)."""
     acc = defaultdict(float)
-    names = {}
+    names, grids = {}, {}
     with open(path) as f:
         for r in csv.DictReader(f):
             if r["Counter_Name"] != counter:
@@ -115,9 +116,10 @@ def counters_by_dispatch(path: str, counter: str):
             d = int(r["Dispatch_Id"])
             acc[d] += float(r["Counter_Value"])
             names[d] = short_name(r["Kernel_Name"])
+            grids[d] = int(r["Grid_Size"])
     out = defaultdict(list)
     for d in sorted(acc):
-        out[names[d]].append((d, acc[d]))
+        out[names[d]].append((d, acc[d], grids[d]))
     return out
 
 
@@ -126,7 +128,7 @@ def _copy_calibration(by_kernel, copy_count: int):
     before the first dispatch of any other kernel (the program makes them first and
     then launches a one-element fill).  A copy split over several dispatches is
     summed whole."""
-    order = sorted((d, name, v) for name, vals in by_kernel.items() for d, v in vals)
+    order = sorted((d, name, v) for name, vals in by_kernel.items() for d, v, _ in vals)
     lead = []
     for d, name, v in order:
         if COPY_KERNEL not in name:
@@ -142,13 +144,17 @@ def _copy_calibration(by_kernel, copy_count: int):
     return sum(copies) / copy_count
 
 
-def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int, copy_count: int = 3):
+def traffic(fetch_csv: str, write_csv: str, kernel: str, copy_bytes: int, copy_count: int = 3,
+            grid: int | None = None):
+    """grid: only the kernel's dispatches of this grid size (work-items), when one
+    program launches it at several shapes."""
     fetch = counters_by_dispatch(fetch_csv, "FETCH_SIZE")
     write = counters_by_dispatch(write_csv, "WRITE_SIZE")
     copy_fetch = _copy_calibration(fetch, copy_count)
     copy_write = _copy_calibration(write, copy_count)
-    kf = [v for name, vals in fetch.items() if name == kernel for _, v in vals]
-    kw = [v for name, vals in write.items() if name == kernel for _, v in vals]
+    keep = lambda g: grid is None or g == grid
+    kf = [v for name, vals in fetch.items() if name == kernel for _, v, g in vals if keep(g)]
+    kw = [v for name, vals in write.items() if name == kernel for _, v, g in vals if keep(g)]
     if not kf or not kw:
         raise SystemExit(f"kernel {kernel!r} not in the counter files (have {sorted(fetch)})")
     copy_kib = copy_bytes / 1024.0
@@ -208,12 +214,15 @@ SQ_COUNTERS = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "S
 N_XCD, N_SIMD = 8, 1024  # MI355X: GRBM_GUI_ACTIVE sums the 8 XCDs; 256 CUs x 4 SIMDs
 
 
-def counters(path: str):
-    """Per kernel: launches and the per-launch average of every counter in SQ_COUNTERS."""
+def counters(path: str, grid: int | None = None):
+    """Per kernel: launches and the per-launch average of every counter in
+    SQ_COUNTERS (only dispatches of `grid` work-items, if given)."""
     per = defaultdict(lambda: defaultdict(float))
     names = {}
     with open(path) as f:
         for r in csv.DictReader(f):
+            if grid is not None and int(r["Grid_Size"]) != grid:
+                continue
             d = int(r["Dispatch_Id"])
             per[d][r["Counter_Name"]] += float(r["Counter_Value"])
             names[d] = short_name(r["Kernel_Name"])
@@ -225,8 +234,8 @@ def counters(path: str):
             for k, cs in out.items()}
 
 
-def counters_markdown(path: str, commands, kernels, title: str) -> str:
-    cs = counters(path)
+def counters_markdown(path: str, commands, kernels, title: str, grid: int | None = None) -> str:
+    cs = counters(path, grid)
     out = [f"# {title}", "", "Made by:", "", "```", *commands, "```", "",
            "Per launch (average over launches). cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs);",
            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); VALU/MFMA counts the non-MFMA vector",
@@ -262,6 +271,7 @@ def main(argv=None):
     t.add_argument("--copy-mib", type=int, required=True)
     t.add_argument("--copy-count", type=int, default=3)
     t.add_argument("--algorithmic-bytes", type=int)
+    t.add_argument("--grid", type=int, help="only dispatches of this grid size (work-items)")
     t.add_argument("--command", action="append", default=[])
     t.add_argument("--out", required=True)
     c = sub.add_parser("counters")
@@ -269,14 +279,17 @@ def main(argv=None):
     c.add_argument("--kernel", action="append", required=True)
     c.add_argument("--command", action="append", default=[])
     c.add_argument("--title", default="MFMA utilisation from SQ counters")
+    c.add_argument("--grid", type=int, help="only dispatches of this grid size (work-items)")
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         text = stats_markdown(a.csv, a.command, a.top, a.title)
     elif a.cmd == "counters":
-        text = counters_markdown(a.csv, a.command, a.kernel, a.title)
+        text = counters_markdown(a.csv, a.command, a.kernel, a.title, a.grid)
     else:
-        tr = traffic(a.fetch, a.write, a.kernel, a.copy_mib << 20, a.copy_count)
+        tr = traffic(a.fetch, a.write, a.kernel, a.copy_mib << 20, a.copy_count, a.grid)
+        if a.grid is not None:
+            tr["grid_size"] = a.grid
         text = traffic_markdown(tr, a.workload, a.command, a.algorithmic_bytes)
     with open(a.out, "w") as f:
         f.write(text)
