@@ -17,6 +17,8 @@ namespace {
 thread_local std::string g_last_error;
 constexpr int64_t kPosLimit = int64_t(1) << 31;
 constexpr int64_t kNoLowerBound = std::numeric_limits<int64_t>::min() / 4;
+// Largest query head count (keeps the kernels' 32-bit tile byte offsets in range).
+constexpr int kMaxHeads = 8192;
 }  // namespace
 
 void set_error(const std::string& msg) { g_last_error = msg; }
@@ -49,6 +51,8 @@ cp_status validate_problem(const cp_attn_problem* p, bool device_docs) {
     if (!p) return fail(CP_ERR_INVALID_ARG, "problem is NULL");
     if (p->hq <= 0 || p->hkv <= 0) return fail(CP_ERR_INVALID_ARG, "head counts must be positive");
     if (p->hq % p->hkv) return fail(CP_ERR_INVALID_ARG, "hq must be a multiple of hkv");
+    // tiles are addressed with 32-bit byte offsets: 64 rows of hq * head_dim bf16 stay far below 2^31
+    if (p->hq > kMaxHeads) return fail(CP_ERR_UNSUPPORTED, "hq above " + std::to_string(kMaxHeads));
     if (p->head_dim != 64 && p->head_dim != 128) return fail(CP_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
     if (!std::isfinite(p->scale)) return fail(CP_ERR_INVALID_ARG, "scale must be finite");
     if (p->q_rows < 0 || p->kv_rows < 0 || p->q_rows >= kPosLimit || p->kv_rows >= kPosLimit)

@@ -87,7 +87,7 @@ typedef struct cp_segment {
  * the window cuts must not be marked FULL: cp_step_masks_window classifies
  * ring steps accordingly.  window = 0: no window. */
 typedef struct cp_attn_problem {
-    int32_t hq, hkv, head_dim;
+    int32_t hq, hkv, head_dim;/* hq <= 8192, a multiple of hkv; head_dim 64 or 128 */
     float scale;              /* softmax scale, normally 1/sqrt(head_dim) */
     int64_t q_rows;           /* rows of the local query tensor */
     int64_t kv_rows;          /* rows of the KV block tensor */

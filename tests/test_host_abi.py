@@ -134,6 +134,8 @@ def test_validation_rejects_bad_problems(lib):
     assert status(masks=[[7, F], [F, F]]) == cpattn.CP_ERR_INVALID_ARG
     assert status(masks=[[cpattn.CP_MASK_DOC, F], [F, F]]) == cpattn.CP_ERR_INVALID_ARG  # no cu_seqlens
     assert status(scale=float("inf")) == cpattn.CP_ERR_INVALID_ARG
+    assert status(hq=16384, hkv=8) == cpattn.CP_ERR_UNSUPPORTED
+    assert status(hq=8192, hkv=8) == cpattn.CP_OK
     # device entry points validate before any HIP call: these return without launching
     p = cpattn.make_problem(**dict(good, head_dim=80))
     assert lib.cp_attn_fwd_step(ctypes.byref(p), None, None, None, None, None, None, None) == cpattn.CP_ERR_UNSUPPORTED
@@ -157,6 +159,10 @@ def test_validation_rejects_bad_problems(lib):
                                 None) == cpattn.CP_ERR_INVALID_ARG
     assert lib.cp_merge_partials(ok, ok, bad, ok, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
     assert lib.cp_attn_bwd_prep(ok, ok, bad, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
+    # a KV segment of 1 GiB or more (2^20 keys x 8 heads x 128 dims x 2 bytes) is refused
+    big = cpattn.make_problem(32, 8, 128, 0.1, 64, 1 << 20, [(0, 1 << 21, 64)], [(0, 0, 1 << 20)], [[F, F], [F, F]])
+    assert lib.cp_attn_fwd_step(ctypes.byref(big), ok, ok, ok, ok, ok, None, None) == cpattn.CP_ERR_UNSUPPORTED
+    assert b"1 GiB" in lib.cp_last_error()
 
 
 def test_clock_probe_arguments(lib):
