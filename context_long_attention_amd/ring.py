@@ -15,8 +15,6 @@ memory, streams and events.
 """
 from __future__ import annotations
 
-import dataclasses
-
 import numpy as np
 import torch
 
@@ -26,13 +24,6 @@ from .inputs import Workload
 
 class RingScheduleError(RuntimeError):
     """A ring schedule that does not visit every source rank exactly once."""
-
-
-@dataclasses.dataclass
-class StepResult:
-    step: int
-    source: int
-    masks: list
 
 
 def check_schedule(cp_size: int, sources) -> None:
