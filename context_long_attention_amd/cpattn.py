@@ -23,9 +23,9 @@ CP_TILE_SKIP, CP_TILE_PARTIAL, CP_TILE_FULL = 0, 1, 2
 # Every symbol include/cpattn.h declares.
 EXPORTS = (
     "cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition_zigzag", "cp_ring_source",
-    "cp_step_masks", "cp_step_masks_window", "cp_tile_shape", "cp_block_map_size", "cp_block_map", "cp_count_pairs",
-    "cp_bwd_kv_split", "cp_attn_fwd_step", "cp_merge_partials", "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step",
-    "cp_debug_clock_probe",
+    "cp_step_masks", "cp_step_masks_window", "cp_tile_shape", "cp_block_map_size", "cp_block_map",
+    "cp_count_pairs", "cp_bwd_kv_split", "cp_merge_partials_n", "cp_attn_fwd_step", "cp_merge_partials",
+    "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step", "cp_debug_clock_probe",
 )
 
 
@@ -81,6 +81,7 @@ def lib():
             "cp_bwd_kv_split": ([P, i32, vp], i32),
             "cp_attn_fwd_step": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
             "cp_merge_partials": ([f32p, f32p, f32p, f32p, i64, i32, i32, vp], i32),
+            "cp_merge_partials_n": ([f32p, f32p, vp, vp, i32, i64, i32, i32, vp], i32),
             "cp_attn_fwd_step_merge": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
             "cp_debug_clock_probe": ([vp, i64], i32),
             "cp_attn_bwd_prep": ([vp, f32p, f32p, i64, i32, i32, vp], i32),
@@ -212,6 +213,16 @@ def cp_attn_fwd_step(p: cp_attn_problem, q, k, v, o_step, lse_step, tile_map=Non
 def cp_merge_partials(o_acc, lse_acc, o_step, lse_step, rows, heads, head_dim, stream=None):
     _check(lib().cp_merge_partials(_ptr(o_acc), _ptr(lse_acc), _ptr(o_step), _ptr(lse_step), rows, heads,
                                    head_dim, _stream(stream)))
+
+
+def cp_merge_partials_n(o_out, lse_out, o_parts, lse_parts, rows, heads, head_dim, stream=None):
+    """Merge the partials in the lists o_parts / lse_parts (same rows, disjoint keys) into o_out / lse_out."""
+    n = len(o_parts)
+    if len(lse_parts) != n:
+        raise ValueError("o_parts and lse_parts differ in length")
+    op = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in o_parts])
+    lp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in lse_parts])
+    _check(lib().cp_merge_partials_n(_ptr(o_out), _ptr(lse_out), op, lp, n, rows, heads, head_dim, _stream(stream)))
 
 
 def cp_attn_fwd_step_merge(p: cp_attn_problem, q, k, v, o_acc, lse_acc, tile_map=None, stream=None):

@@ -12,6 +12,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <string>
 
 #include "internal.h"
 
@@ -53,6 +54,48 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(float* __restrict__ o_a
     }
     *reinterpret_cast<f32x4*>(o_acc + pair * D + sub * 4) = out;
     if (sub == 0) lse_acc[li] = lnew;
+}
+
+// The N-way merge: the partials of one query row over n disjoint key sets (an
+// owner merging what Pass Q's all-to-all delivers), read once each.
+constexpr int kMaxParts = 64;
+struct MergeNParams {
+    const float* o[kMaxParts];
+    const float* lse[kMaxParts];
+    float* o_out;
+    float* lse_out;
+    int64_t rows;
+    int32_t heads, n;
+};
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_n_kernel(const MergeNParams p) {
+    constexpr int LPG = D / 4;
+    const int64_t gidx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+    const int64_t pair = gidx / LPG;
+    const int sub = int(gidx % LPG);
+    if (pair >= p.rows * p.heads) return;
+    const int64_t row = pair / p.heads;
+    const int head = int(pair % p.heads);
+    const int64_t li = (int64_t)head * p.rows + row;
+    const int64_t oi = pair * D + sub * 4;
+    float mx = -INFINITY;
+    for (int i = 0; i < p.n; ++i) mx = fmaxf(mx, p.lse[i][li]);
+    f32x4 out = {0.f, 0.f, 0.f, 0.f};
+    float lnew = -INFINITY;
+    if (mx != -INFINITY) {
+        // weights e^(L_i - max) in (0, 1], one of them 1: the sum is >= 1
+        float sum = 0.f;
+        for (int i = 0; i < p.n; ++i) {
+            const float wgt = __expf(p.lse[i][li] - mx);
+            sum += wgt;
+            out += *reinterpret_cast<const f32x4*>(p.o[i] + oi) * wgt;
+        }
+        out *= 1.f / sum;
+        lnew = mx + __logf(sum);
+    }
+    *reinterpret_cast<f32x4*>(p.o_out + oi) = out;
+    if (sub == 0) p.lse_out[li] = lnew;
 }
 
 template <int D>
@@ -104,6 +147,41 @@ extern "C" cp_status cp_merge_partials(float* o_acc, float* lse_acc, const float
     else
         hipLaunchKernelGGL(merge_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, o_acc, lse_acc, o_step,
                            lse_step, rows, heads);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
+    return CP_OK;
+}
+
+extern "C" cp_status cp_merge_partials_n(float* o_out, float* lse_out, const float* const* o_parts,
+                                         const float* const* lse_parts, int32_t n_parts, int64_t rows, int32_t heads,
+                                         int32_t head_dim, hipStream_t stream) {
+    if (rows < 0 || heads <= 0) return fail(CP_ERR_INVALID_ARG, "bad sizes");
+    if (head_dim != 64 && head_dim != 128) return fail(CP_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+    if (n_parts < 1 || n_parts > kMaxParts)
+        return fail(CP_ERR_INVALID_ARG, "n_parts must be in [1, " + std::to_string(kMaxParts) + "]");
+    if (rows == 0) return CP_OK;
+    if (!o_out || !lse_out || !o_parts || !lse_parts) return fail(CP_ERR_INVALID_ARG, "NULL pointer");
+    MergeNParams prm = {};
+    for (int i = 0; i < n_parts; ++i) {
+        if (!o_parts[i] || !lse_parts[i]) return fail(CP_ERR_INVALID_ARG, "NULL part pointer");
+        if (!all_aligned16({o_parts[i], lse_parts[i]}))
+            return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+        prm.o[i] = o_parts[i];
+        prm.lse[i] = lse_parts[i];
+    }
+    if (!all_aligned16({o_out, lse_out})) return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+    prm.o_out = o_out;
+    prm.lse_out = lse_out;
+    prm.rows = rows;
+    prm.heads = heads;
+    prm.n = n_parts;
+    const int64_t threads = rows * heads * (head_dim / 4);
+    const int64_t grid = ceil_div(threads, kThreads);
+    if (grid > 0x7fffffff) return fail(CP_ERR_UNSUPPORTED, "too large");
+    if (head_dim == 128)
+        hipLaunchKernelGGL(merge_n_kernel<128>, dim3(grid), dim3(kThreads), 0, stream, prm);
+    else
+        hipLaunchKernelGGL(merge_n_kernel<64>, dim3(grid), dim3(kThreads), 0, stream, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("merge launch: ") + hipGetErrorString(e));
     return CP_OK;

@@ -100,10 +100,9 @@ class PassQRank:
         that every rank computed for this owner's rows (``received``: list of
         (O_t, LSE_t)).  Returns the owner's (O, LSE)."""
         w, rows = self.w, 2 * self.c
-        o = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=self.device)
-        lse = torch.full((w.hq, rows), float("-inf"), dtype=torch.float32, device=self.device)
-        for o_t, l_t in received:
-            cpattn.cp_merge_partials(o, lse, o_t, l_t, rows, w.hq, w.dim)
+        o = torch.empty((rows, w.hq, w.dim), dtype=torch.float32, device=self.device)
+        lse = torch.empty((w.hq, rows), dtype=torch.float32, device=self.device)
+        cpattn.cp_merge_partials_n(o, lse, [x[0] for x in received], [x[1] for x in received], rows, w.hq, w.dim)
         return o, lse
 
 

@@ -208,6 +208,22 @@ cp_status cp_attn_fwd_step(const cp_attn_problem* p, const void* q, const void* 
 cp_status cp_merge_partials(float* o_acc, float* lse_acc, const float* o_step, const float* lse_step,
                             int64_t rows, int32_t heads, int32_t head_dim, hipStream_t stream);
 
+/* Merge of n_parts (1..64) partial outputs of the same rows over disjoint key
+ * sets, each read once: what an owner does with the partials Pass Q's
+ * all-to-all delivers to it ("... Million-Token Inference", section "Ring
+ * Attention Algorithms": with Pass Q the partial outputs are sent to the
+ * ranks that own the queries, which merge them).  L = ln sum_i e^(L_i);
+ * O = sum_i e^(L_i - L) O_i; all -inf gives (0, -inf).  o_parts / lse_parts
+ * are HOST arrays of n_parts device pointers, each part laid out as in
+ * cp_merge_partials.  o_out / lse_out may be the first part's buffers (in
+ * place), but no other part's.
+ *   o_out    device fp32 [rows, heads, head_dim]   out
+ *   lse_out  device fp32 [heads, rows]             out
+ * INVALID_ARG on n_parts outside [1, 64] or a NULL or misaligned pointer. */
+cp_status cp_merge_partials_n(float* o_out, float* lse_out, const float* const* o_parts,
+                              const float* const* lse_parts, int32_t n_parts, int64_t rows, int32_t heads,
+                              int32_t head_dim, hipStream_t stream);
+
 /* Forward of one ring step fused with the merge of its partial output into the
  * running accumulator ("... Million-Token Inference", section "Ring Attention
  * Algorithms": the partial outputs are merged as the KV blocks circulate).

@@ -250,6 +250,41 @@ def test_merge_kernel_matches_oracle():
     np.testing.assert_allclose(got_l[np.isfinite(rl)], rl[np.isfinite(rl)], atol=1e-5)
 
 
+@pytest.mark.parametrize("n,d", [(1, 128), (3, 64), (8, 128), (64, 64)])
+def test_merge_n_matches_pairwise_oracle(n, d):
+    """The N-way merge equals folding the parts one by one with the oracle's
+    pairwise merge, including rows that are -inf in some or all parts; the output
+    may be the first part's buffers."""
+    from context_long_attention_amd import cpattn
+    rng = np.random.default_rng(n)
+    rows, hq = 257, 3
+    os_ = [rng.standard_normal((rows, hq, d)) for _ in range(n)]
+    ls = [rng.standard_normal((hq, rows)) * 6 for _ in range(n)]
+    for i in range(n):
+        dead = rng.random((hq, rows)) < 0.3
+        dead[:, :4] = True  # rows 0..3 are -inf in every part
+        ls[i][dead] = -np.inf
+        os_[i][np.transpose(dead)] = 0.0
+    ro = np.zeros((rows, hq, d))
+    rl = np.full((hq, rows), -np.inf)
+    for o_i, l_i in zip(os_, ls):
+        ro, rl = oracle.merge(ro, rl, np.float32(o_i).astype(np.float64), np.float32(l_i).astype(np.float64))
+    t = lambda x: torch.tensor(x, dtype=torch.float32, device="cuda")
+    o_parts, l_parts = [t(x) for x in os_], [t(x) for x in ls]
+    out_o = torch.full((rows, hq, d), 7.0, device="cuda")
+    out_l = torch.full((hq, rows), 7.0, device="cuda")
+    cpattn.cp_merge_partials_n(out_o, out_l, o_parts, l_parts, rows, hq, d)
+    # in place on part 0
+    cpattn.cp_merge_partials_n(o_parts[0], l_parts[0], o_parts, l_parts, rows, hq, d)
+    torch.cuda.synchronize()
+    for go, gl, what in ((out_o, out_l, "out"), (o_parts[0], l_parts[0], "in place")):
+        np.testing.assert_allclose(go.cpu().numpy(), ro, atol=2e-5, err_msg=what)
+        g = gl.cpu().numpy()
+        assert np.array_equal(np.isneginf(g), np.isneginf(rl)), what
+        np.testing.assert_allclose(g[np.isfinite(rl)], rl[np.isfinite(rl)], atol=2e-5, err_msg=what)
+    assert torch.all(out_o[:4] == 0).item()
+
+
 def _sampled_rows(local, c, n_extra, seed):
     rng = np.random.default_rng(seed)
     edge = [0, 1, 2, c - 1, c, c + 1, local - 2, local - 1]

@@ -143,6 +143,9 @@ def test_validation_rejects_bad_problems(lib):
                                 None) == cpattn.CP_ERR_UNSUPPORTED
     assert lib.cp_merge_partials(None, None, None, None, -1, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
     assert lib.cp_merge_partials(None, None, None, None, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
+    for n in (0, 65):
+        assert lib.cp_merge_partials_n(None, None, None, None, n, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_merge_partials_n(None, None, None, None, 2, 10, 4, 96, None) == cpattn.CP_ERR_UNSUPPORTED
     assert lib.cp_attn_bwd_prep(None, None, None, 10, 4, 72, None) == cpattn.CP_ERR_UNSUPPORTED
     assert b"head_dim" in lib.cp_last_error()
     # misaligned tensor pointers are rejected before any launch (never dereferenced;
@@ -158,6 +161,9 @@ def test_validation_rejects_bad_problems(lib):
     assert lib.cp_attn_bwd_step(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, ok, bad,
                                 None) == cpattn.CP_ERR_INVALID_ARG
     assert lib.cp_merge_partials(ok, ok, bad, ok, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
+    arr = lambda *a: (ctypes.c_void_p * len(a))(*a)
+    assert lib.cp_merge_partials_n(ok, ok, arr(ok, bad), arr(ok, ok), 2, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_merge_partials_n(ok, ok, arr(ok, None), arr(ok, ok), 2, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
     assert lib.cp_attn_bwd_prep(ok, ok, bad, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
     # a KV segment of 1 GiB or more (2^20 keys x 8 heads x 128 dims x 2 bytes) is refused
     big = cpattn.make_problem(32, 8, 128, 0.1, 64, 1 << 20, [(0, 1 << 21, 64)], [(0, 0, 1 << 20)], [[F, F], [F, F]])
