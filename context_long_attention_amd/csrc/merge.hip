@@ -80,12 +80,14 @@ __global__ __launch_bounds__(kThreads) void merge_n_kernel(const MergeNParams p)
     const int64_t li = (int64_t)head * p.rows + row;
     const int64_t oi = pair * D + sub * 4;
     float mx = -INFINITY;
+#pragma unroll 4
     for (int i = 0; i < p.n; ++i) mx = fmaxf(mx, p.lse[i][li]);
     f32x4 out = {0.f, 0.f, 0.f, 0.f};
     float lnew = -INFINITY;
     if (mx != -INFINITY) {
         // weights e^(L_i - max) in (0, 1], one of them 1: the sum is >= 1
         float sum = 0.f;
+#pragma unroll 4
         for (int i = 0; i < p.n; ++i) {
             const float wgt = __expf(p.lse[i][li] - mx);
             sum += wgt;
