@@ -298,22 +298,34 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
             sb[h2] = __builtin_convertvector(b, bf16x8);
         }
 
-        // dV^T += dO^T P and dK^T += Q^T dS (M = dims, N = keys, K = queries 16 s2 + 4hl + {0..3, 8..11})
+        // dV^T += dO^T P and dK^T += Q^T dS (M = dims, N = keys, K = queries 16 s2 + 4hl + {0..3, 8..11});
+        // MFMA m: pair e = m / 2 (s2 = e / DB, db = e % DB), dV for even m and dK for odd m, its A
+        // operand read two MFMAs ahead
+        auto t_operand = [&](int m) -> bf16x8 {
+            const int e = m >> 1;
+            const char* base = (m & 1) ? qsl : osl;
+            const int o = t_lane + L::off(16 * (e / DB), 32 * (e % DB));
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(base + o + L::off(8, 0)));
+            const s16x8 a = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            return __builtin_bit_cast(bf16x8, a);
+        };
+        bf16x8 ta[3];
+        ta[0] = t_operand(0);
+        ta[1] = t_operand(1);
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-#pragma unroll
-            for (int db = 0; db < DB; ++db) {
-                const int o = t_lane + L::off(16 * s2, 32 * db);
-                const s16x4 ol = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(osl + o));
-                const s16x4 oh = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(osl + o + L::off(8, 0)));
-                const s16x8 ao = {ol[0], ol[1], ol[2], ol[3], oh[0], oh[1], oh[2], oh[3]};
-                dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, ao), pb[s2], dva[db],
-                                                                   0, 0, 0);
-                const s16x4 ql4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qsl + o));
-                const s16x4 qh4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(qsl + o + L::off(8, 0)));
-                const s16x8 aq = {ql4[0], ql4[1], ql4[2], ql4[3], qh4[0], qh4[1], qh4[2], qh4[3]};
-                dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, aq), sb[s2], dka[db],
-                                                                   0, 0, 0);
+        for (int m = 0; m < 4 * DB; ++m) {
+            if (m + 2 < 4 * DB) {
+                ta[(m + 2) % 3] = t_operand(m + 2);
+                order_memory();
+            }
+            const int e = m >> 1, s2 = e / DB, db = e % DB;
+            if ((m & 1) == 0) {
+                dva[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m % 3], pb[s2], dva[db], 0, 0, 0);
+                pin(dva[db]);
+            } else {
+                dka[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ta[m % 3], sb[s2], dka[db], 0, 0, 0);
+                pin(dka[db]);
             }
         }
         if constexpr (decltype(bar)::value) ring_barrier<0>();
@@ -342,6 +354,10 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     // of 32 rows: every wave stages its 32 rows, half of the dims in its query
     // slot and half in its dO slot (free once the ring has drained), as rows of
     // D/2 floats with 16-byte chunks XOR-swizzled by row.
+    // lane-derived values of the epilogue recomputed here (from the lane count, not
+    // from registers kept through the loop)
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int ql_e = lane_e & 31, hl_e = lane_e >> 5, kk_e = 32 * wave + ql_e;
     if (p.kv_split > 1) {
         constexpr int HALF = D / 2, NCH = HALF / 4, ROWB = HALF * 4;
         static_assert(32 * ROWB <= L::BYTES, "a ring slot holds half of a wave's rows");
@@ -358,11 +374,11 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
                 for (int db = 0; db < DB; ++db)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
-                        const int d = 32 * db + 8 * i + 4 * hl;
+                        const int d = 32 * db + 8 * i + 4 * hl_e;
                         const int ch = (d % HALF) / 4;
                         const f32x4 x = {acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul, acc[db][4 * i + 2] * mul,
                                          acc[db][4 * i + 3] * mul};
-                        *reinterpret_cast<f32x4*>(st[d / HALF] + ql * ROWB + ((ch ^ (ql % NCH)) * 16)) = x;
+                        *reinterpret_cast<f32x4*>(st[d / HALF] + ql_e * ROWB + ((ch ^ (ql_e % NCH)) * 16)) = x;
                     }
                 __syncthreads();
                 float* out = t ? p.dv : p.dk;
@@ -371,7 +387,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
                 for (int h = 0; h < 2; ++h)
 #pragma unroll 4
                     for (int r0 = 0; r0 < 32; r0 += RPI) {
-                        const int r = r0 + lane / HALF, dl = lane % HALF;
+                        const int r = r0 + lane_e / HALF, dl = lane_e % HALF;
                         const float x = *reinterpret_cast<const float*>(st[h] + r * ROWB +
                                                                         (((dl / 4) ^ (r % NCH)) * 16) + 4 * (dl % 4));
                         if (32 * wave + r < kcount) unsafeAtomicAdd(out + row0 + (int64_t)r * kv_stride + h * HALF + dl, x);
@@ -379,13 +395,13 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
                 __syncthreads();
             }
         }
-    } else if (key_valid) {
-        const int64_t base = (int64_t)(key_row0 + kk) * kv_stride + (int64_t)g * D;
+    } else if (kk_e < kcount) {
+        const int64_t base = (int64_t)(key_row0 + kk_e) * kv_stride + (int64_t)g * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int d0 = 32 * db + 8 * i + 4 * hl;
+                const int d0 = 32 * db + 8 * i + 4 * hl_e;
                 const f32x4 kv4 = {dka[db][4 * i] * p.scale, dka[db][4 * i + 1] * p.scale,
                                    dka[db][4 * i + 2] * p.scale, dka[db][4 * i + 3] * p.scale};
                 const f32x4 vv4 = {dva[db][4 * i], dva[db][4 * i + 1], dva[db][4 * i + 2], dva[db][4 * i + 3]};
