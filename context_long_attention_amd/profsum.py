@@ -1,6 +1,6 @@
 """Short text summaries of rocprofv3 CSV output, and the traffic lookup bench.py uses.
 
-Three summaries are produced (all markdown with the exact commands that made
+Four summaries are produced (all markdown with the exact commands that made
 them):
 
 * ``stats``: the per-kernel table of a ``rocprofv3 --kernel-trace --stats
@@ -14,6 +14,8 @@ them):
   only while those sources are unchanged.
 * ``counters``: MFMA utilisation and instruction mix per kernel from one
   ``--pmc`` pass over the SQ counters listed in ``SQ_COUNTERS``.
+* ``dispatches``: the individual dispatches of chosen kernels from a
+  ``--kernel-trace`` run, in order, with their workgroup counts and durations.
 
 Usage::
 
@@ -101,6 +103,31 @@ def stats_markdown(path: str, commands, top: int = 12, title: str | None = None)
     for r in rows[:top]:
         out.append(f"| `{r['name']}` | {r['calls']} | {r['total_ms']:.3f} | {r['avg_ms']:.4f} | {r['min_ms']:.4f} | "
                    f"{r['max_ms']:.4f} | {r['pct']:.2f} |")
+    return "\n".join(out) + "\n"
+
+
+def dispatch_rows(path: str, match, last: int | None = None):
+    """Dispatches of a ``--kernel-trace`` CSV whose kernel short name contains one of
+    the ``match`` strings, in dispatch order: (id, name, workgroups, ms); the last
+    ``last`` of them if given."""
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            name = short_name(r["Kernel_Name"])
+            if not any(m in name for m in match):
+                continue
+            wgs = int(r["Grid_Size_X"]) // max(1, int(r["Workgroup_Size_X"]))
+            ms = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6
+            rows.append((int(r["Dispatch_Id"]), name, wgs, ms))
+    rows.sort()
+    return rows[-last:] if last else rows
+
+
+def dispatches_markdown(path: str, commands, match, last, title: str) -> str:
+    out = [f"# {title}", "", "Made by:", "", "```", *commands, "```", "",
+           "| dispatch | kernel | workgroups | ms |", "|---:|---|---:|---:|"]
+    for d, name, wgs, ms in dispatch_rows(path, match, last):
+        out.append(f"| {d} | `{name}` | {wgs} | {ms:.4f} |")
     return "\n".join(out) + "\n"
 
 
@@ -274,6 +301,13 @@ def main(argv=None):
     t.add_argument("--grid", type=int, help="only dispatches of this grid size (work-items)")
     t.add_argument("--command", action="append", default=[])
     t.add_argument("--out", required=True)
+    d = sub.add_parser("dispatches")
+    d.add_argument("--csv", required=True, help="the *_kernel_trace.csv of a --kernel-trace run")
+    d.add_argument("--match", action="append", required=True, help="substring of the kernel names to list")
+    d.add_argument("--last", type=int, help="only the last N matching dispatches")
+    d.add_argument("--command", action="append", default=[])
+    d.add_argument("--title", default="Kernel dispatches")
+    d.add_argument("--out", required=True)
     c = sub.add_parser("counters")
     c.add_argument("--csv", required=True)
     c.add_argument("--kernel", action="append", required=True)
@@ -284,6 +318,8 @@ def main(argv=None):
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         text = stats_markdown(a.csv, a.command, a.top, a.title)
+    elif a.cmd == "dispatches":
+        text = dispatches_markdown(a.csv, a.command, a.match, a.last, a.title)
     elif a.cmd == "counters":
         text = counters_markdown(a.csv, a.command, a.kernel, a.title, a.grid)
     else:
