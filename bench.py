@@ -115,6 +115,27 @@ def probe_clock(torch, one_step):
                       "of an extra untimed pass"}
 
 
+def gemm_reference(torch, n=16384, reps=10):
+    """Context for the power-capped clock, not part of the measured path: the
+    vendor library's dense bf16 GEMM (torch.matmul, n^3) on the same GPU in the
+    same run, as TFLOP/s and as a fraction of the same bf16 peak."""
+    a = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    b = torch.randn((n, n), device="cuda", dtype=torch.bfloat16)
+    torch.matmul(a, b)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        torch.matmul(a, b)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / reps
+    t = tflops(2.0 * n ** 3, ms)
+    return {"kind": "vendor library dense GEMM on the same GPU (context, not this library's code)",
+            "shape": f"bf16 [{n}, {n}] x [{n}, {n}], torch.matmul", "tflops": round(t, 2),
+            "pct_bf16_peak": round(100 * t / BF16_PEAK_TFLOPS, 2), "ms": round(ms, 3)}
+
+
 def cpu_baseline(w, rank, heads):
     """The float64 oracle on a bounded sample: ``heads`` query heads of the GQA group
     of KV head 0, every ring step of the rank, every local row."""
@@ -471,6 +492,8 @@ def main():
     ap.add_argument("--no-window", action="store_true", help="skip the sliding-window layer leg")
     ap.add_argument("--no-large", action="store_true", help="skip the Llama-3-405B prefill leg")
     ap.add_argument("--no-packed", action="store_true", help="skip the packed-document training leg")
+    ap.add_argument("--no-gemm-reference", action="store_true",
+                    help="skip the same-box vendor GEMM reference (context for the power-capped clock)")
     ap.add_argument("--window-workload", default="llama3_8b_window4k")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="first make 3 device-to-device copies of this many MiB (counter calibration)")
@@ -551,6 +574,9 @@ def main():
     if not args.no_window:
         record["sliding_window"] = measure_window(torch, inputs.WORKLOADS[args.window_workload], args.rank,
                                                   max(1, args.steps // 2), 1)
+    if not args.no_gemm_reference:
+        record["gemm_reference"] = gemm_reference(torch)
+        record["gemm_reference"]["attention_over_gemm"] = round(value / record["gemm_reference"]["tflops"], 3)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host (cpu_baseline)")
         record["cpu_baseline"] = cpu_baseline(w, args.rank, args.cpu_heads)
