@@ -99,6 +99,11 @@ RAGGED = [
     ("g8_d128", 2 * 2 * 130, 2, 8, 1, 128),
     ("g3_d64", 2 * 2 * 70, 2, 6, 2, 64),
     ("r16_c256", 2 * 16 * 256, 16, 8, 2, 128),
+    # Hkv a multiple of 8 with several head blocks per KV head: the work order renumbers
+    # head blocks so a KV head's blocks share an XCD (2 and 4 blocks per KV head)
+    ("hkv8_g8_d128", 2 * 2 * 160, 2, 64, 8, 128),
+    ("hkv8_g16_d128", 2 * 2 * 96, 2, 128, 8, 128),
+    ("hkv16_g4_d64", 2 * 2 * 72, 2, 64, 16, 64),
 ]
 
 
