@@ -139,3 +139,66 @@ def test_head_sharded_call():
         ro, rl = ov.head_sharded_attention(q64, k64, v64, list(range(hq))[qh], list(range(hkv))[kvh], d ** -0.5)
         assert_o_close(o.cpu().numpy(), ro, f"head-sharded O device {dev_i}")
         assert_lse_close(lse.cpu().numpy(), rl, f"head-sharded LSE device {dev_i}")
+
+
+@pytest.mark.timeout(900)
+def test_pass_q_llama3_8b_full_size_sampled():
+    """Pass Q at the Llama-3-8B forward shape the bench times (S=128K, CP=8,
+    Hq=32, Hkv=8, D=128): every rank's K/V against every visiting Q block, then
+    owner 0's merge of the 8 partials it receives, on sampled rows against the
+    oracle over every key."""
+    from context_long_attention_amd.variants import PassQRank
+    from tests.gpu_common import RankInputs, _to_device, sampled_rows
+    w = inputs.WORKLOADS["llama3_8b_fwd"]
+    R, c, owner = w.cp, w.chunk, 0
+    note(f"pass-q full size {w.name} owner {owner}")
+    inp = RankInputs(w, owner)  # the owner's Q and every rank's K/V
+    q_dev = {owner: inp.q}
+    for r in range(R):
+        if r != owner:
+            q_dev[r] = _to_device(inputs.bf16_bits(inputs.chunks_normal(inputs.SEED_Q, oracle.zigzag_chunks(R, r), c,
+                                                                        w.hq, w.dim)))
+    received = []
+    for r in range(R):
+        k, v = inp.kv[r]
+        parts = PassQRank(w, r).forward(k, v, q_dev.__getitem__)
+        received += [(o_t, l_t) for s, o_t, l_t in parts if s == owner]
+        del parts
+    assert len(received) == R
+    o, lse = PassQRank(w, owner).restore(received)
+    torch.cuda.synchronize()
+    rows = sampled_rows(w.local, c, 24, 17)
+    ro, rl, _ = oracle.rank_forward(widen(inp.q_bits[rows]), inp.qpos[rows], inp.blocks(range(R)), None, w.scale)
+    assert_o_close(o[rows].cpu().numpy(), ro, "pass-q full-size restored O")
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, "pass-q full-size restored LSE")
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("rank", [0, 7])
+def test_partial_prefill_llama3_8b_full_size_sampled(rank):
+    """Partial prefill at the bench's configuration: 96K cached + 32K new tokens
+    over CP=8 at the Llama-3-8B head shape; the rank's new-token rows (sampled)
+    against every cached key and the new keys before them."""
+    from context_long_attention_amd.variants import PartialPrefillRank
+    from tests.gpu_common import sampled_rows
+    w = inputs.WORKLOADS["llama3_8b_fwd"]
+    R, hq, hkv, d = w.cp, w.hq, w.hkv, w.dim
+    P, N = 3 * w.seq_len // 4, w.seq_len // 4
+    note(f"partial prefill full size P={P} N={N} R={R} rank={rank}")
+    k_bits = inputs.bf16_bits(inputs.chunk_normal(22, 0, P + N, hkv, d))
+    v_bits = inputs.bf16_bits(inputs.chunk_normal(23, 0, P + N, hkv, d))
+    qn_bits = inputs.bf16_bits(inputs.chunk_normal(21, 0, N, hq, d))  # queries of the new tokens, by position - P
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    pp = PartialPrefillRank(P, N, R, hq, hkv, d, rank)
+    parts = {s: ov.partial_prefill_positions(P, N, R, s) for s in range(R)}
+    kv = {s: (dev(k_bits[parts[s][0]]), dev(v_bits[parts[s][0]]), dev(k_bits[parts[s][1]]), dev(v_bits[parts[s][1]]))
+          for s in range(R)}
+    new_r = parts[rank][1]
+    o, lse = pp.forward(dev(qn_bits[new_r - P]), kv.__getitem__)
+    torch.cuda.synchronize()
+    rows = sampled_rows(len(new_r), len(new_r) // 2, 20, rank + 3)
+    blocks = [((widen(k_bits[parts[s][0]]), widen(v_bits[parts[s][0]]), parts[s][0]),
+               (widen(k_bits[parts[s][1]]), widen(v_bits[parts[s][1]]), parts[s][1])) for s in pp.schedule()]
+    ro, rl = ov.partial_prefill_rank(widen(qn_bits[new_r[rows] - P]), new_r[rows], blocks, w.scale)
+    assert_o_close(o[rows].cpu().numpy(), ro, f"partial prefill full-size O rank {rank}")
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, f"partial prefill full-size LSE rank {rank}")
