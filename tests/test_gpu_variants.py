@@ -202,3 +202,39 @@ def test_partial_prefill_llama3_8b_full_size_sampled(rank):
     ro, rl = ov.partial_prefill_rank(widen(qn_bits[new_r[rows] - P]), new_r[rows], blocks, w.scale)
     assert_o_close(o[rows].cpu().numpy(), ro, f"partial prefill full-size O rank {rank}")
     assert_lse_close(lse[:, rows].cpu().numpy(), rl, f"partial prefill full-size LSE rank {rank}")
+
+
+@pytest.mark.timeout(900)
+def test_gathered_and_head_sharded_llama3_8b_full_size_sampled():
+    """The gathered-KV call (rank 0's query share against the whole 128K-token
+    sequence) and the head-sharded call (4 query heads and their KV head over the
+    whole sequence) at the Llama-3-8B shape the bench times, on sampled rows."""
+    from context_long_attention_amd.variants import gathered_forward, head_sharded_forward
+    from tests.gpu_common import sampled_rows
+    w = inputs.WORKLOADS["llama3_8b_fwd"]
+    S, R, c, hq, hkv, d = w.seq_len, w.cp, w.chunk, w.hq, w.hkv, w.dim
+    note(f"gathered and head-sharded full size S={S}")
+    dev = lambda bits: torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).cuda().view(torch.bfloat16)
+    k_bits = inputs.bf16_bits(inputs.chunk_normal(42, 0, S, hkv, d))
+    v_bits = inputs.bf16_bits(inputs.chunk_normal(43, 0, S, hkv, d))
+    k64, v64 = widen(k_bits), widen(v_bits)
+    # gathered KV: rank 0's two zigzag chunks of queries
+    q_bits = inputs.bf16_bits(inputs.chunk_normal(41, 0, 2 * c, hq, d))
+    qpos = oracle.zigzag_positions(S, R, 0)
+    o, lse = gathered_forward(w, 0, dev(q_bits), dev(k_bits), dev(v_bits))
+    torch.cuda.synchronize()
+    rows = sampled_rows(2 * c, c, 20, 9)
+    ro, rl = ov.gathered_attention(widen(q_bits[rows]), qpos[rows], k64, v64, w.scale)
+    assert_o_close(o[rows].cpu().numpy(), ro, "gathered full-size O")
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, "gathered full-size LSE")
+    # head-sharded: Hq/R query heads and Hkv/R KV heads over the whole sequence
+    gh, gk = hq // R, hkv // R
+    qh_bits = inputs.bf16_bits(inputs.chunk_normal(44, 0, S, gh, d))
+    o, lse = head_sharded_forward(dev(qh_bits), dev(k_bits[:, :gk]), dev(v_bits[:, :gk]), w.scale)
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([[0, 1, S // 2, S - 1], np.random.default_rng(10).integers(0, S, 24)]))
+    pos = np.arange(S)
+    ro, rl = oracle.attention_partial(widen(qh_bits[rows]), k64[:, :gk], v64[:, :gk], oracle.visibility(rows, pos),
+                                      w.scale)
+    assert_o_close(o[rows].cpu().numpy(), ro, "head-sharded full-size O")
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, "head-sharded full-size LSE")
