@@ -344,6 +344,22 @@ def measure_variants(torch, w, rank, steps, warmup):
     del kvs
     log(f"partial_prefill: {ms:.3f} ms/step")
 
+    # USP with all-to-all groups of 2: the device's ring over cp/2 groups with half the heads
+    from context_long_attention_amd.ring import RankRing
+    from context_long_attention_amd.variants import usp_share
+    wu = usp_share(w, 2)
+    uq, ukv = make_rank_inputs(torch, wu, rank)
+    pairs = sum(RankRing(wu, rank).step_pairs(t) for t in range(wu.cp))
+    ms, kern = _time_leg(torch, lambda timer: RankRing(wu, rank).forward(uq, ukv.__getitem__, stage=True, timer=timer),
+                         steps, warmup, KernelTimer(torch, "fwd"))
+    fpu = wu.hq * wu.dim * 4
+    out["usp"] = {"workload": f"{w.name} USP share, all-to-all groups of 2: ring of {wu.cp} ranks, Hq={wu.hq}, "
+                              f"Hkv={wu.hkv}, {wu.local} local tokens, rank {rank}",
+                  "tflops": round(tflops(pairs * fpu, ms), 2), "kernel_tflops": round(tflops(pairs * fpu, kern), 2),
+                  "ms_per_step": round(ms, 4)}
+    del uq, ukv
+    log(f"usp: {ms:.3f} ms/step")
+
     # gathered KV (all-gather strategy): the rank's query share against the whole sequence
     q_loc = _dev_normal(torch, (2 * c, w.hq, w.dim), 801)
     k_all = _dev_normal(torch, (w.seq_len, w.hkv, w.dim), 802)

@@ -13,6 +13,11 @@
   token and causally to each other; both the cached prefix and the new tokens
   are split in 2R chunks, rank r holding chunks r and 2R-1-r of each, and the
   ring passes both parts of every rank's KV.
+* USP (all-to-all inside groups of U devices, a ring across the groups) -- same
+  MaxText section: after the all-to-all a device holds Hq/U query heads and
+  Hkv/U KV heads of its group's pooled tokens, and the ring over the R/U groups
+  passes blocks U times larger.  Its attention work is the Pass-KV ring of
+  ``usp_share`` (``RankRing`` unchanged).
 * Gathered KV and head-sharded attention -- "Announcing Long-Context Training on
   TPUs with MaxText Context Parallelism", section "Context Parallelism in
   MaxText": the per-device work of the all-gather strategy (the rank's query
@@ -23,6 +28,8 @@ All arithmetic runs in libcpattn; torch only provides memory, streams and events
 """
 from __future__ import annotations
 
+import dataclasses
+
 import torch
 
 from . import cpattn
@@ -31,6 +38,16 @@ from .ring import _Feeder, check_schedule
 
 # largest KV segment (bytes of one KV tensor) one call may address
 _SPAN_LIMIT = (1 << 30) - 1
+
+
+def usp_share(w: Workload, u: int) -> Workload:
+    """One device's attention work under USP with all-to-all groups of ``u``
+    devices: a Pass-KV ring of w.cp / u ranks over the same sequence, with
+    w.hq / u query heads and w.hkv / u KV heads (u must divide w.cp, w.hq and
+    w.hkv, so each device keeps whole GQA groups)."""
+    if u < 1 or w.cp % u or w.hq % u or w.hkv % u:
+        raise ValueError(f"USP group size {u} must divide cp={w.cp}, hq={w.hq} and hkv={w.hkv}")
+    return dataclasses.replace(w, name=f"{w.name}_usp{u}", cp=w.cp // u, hq=w.hq // u, hkv=w.hkv // u)
 
 
 class PassQRank:

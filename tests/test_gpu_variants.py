@@ -238,3 +238,26 @@ def test_gathered_and_head_sharded_llama3_8b_full_size_sampled():
                                       w.scale)
     assert_o_close(o[rows].cpu().numpy(), ro, "head-sharded full-size O")
     assert_lse_close(lse[:, rows].cpu().numpy(), rl, "head-sharded full-size LSE")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,u,rank", [("small", 2, 0), ("small", 2, 3), ("llama3_8b_fwd", 2, 0)])
+def test_usp_share(name, u, rank):
+    """USP's per-device work (a Pass-KV ring over cp/u ranks with hq/u and hkv/u
+    heads) through the unchanged ring, against the oracle: whole tensors on a small
+    shape, sampled rows at the Llama-3-8B shape the bench times."""
+    from context_long_attention_amd.ring import RankRing
+    from context_long_attention_amd.variants import usp_share
+    from tests.gpu_common import RankInputs, sampled_rows
+    base = inputs.WORKLOADS[name] if name != "small" else inputs.Workload("small", 2 * 8 * 96, 8, 8, 4, 128, False)
+    w = usp_share(base, u)
+    note(f"usp {w.name} cp={w.cp} hq={w.hq} hkv={w.hkv} rank={rank}")
+    inp = RankInputs(w, rank)
+    ring = RankRing(w, rank)
+    o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
+    torch.cuda.synchronize()
+    rows = np.arange(w.local) if name == "small" else sampled_rows(w.local, w.chunk, 24, rank + 31)
+    ro, rl, _ = oracle.rank_forward(widen(inp.q_bits[rows]), inp.qpos[rows], inp.blocks(ring.schedule()), None,
+                                    w.scale)
+    assert_o_close(o[rows].cpu().numpy(), ro, f"usp O {w.name} rank {rank}")
+    assert_lse_close(lse[:, rows].cpu().numpy(), rl, f"usp LSE {w.name} rank {rank}")

@@ -120,3 +120,27 @@ def test_head_sharded_call_is_full_attention_of_its_heads():
         o, lse = variants.head_sharded_attention(q, k, v, qh, kvh, 0.3)
         np.testing.assert_allclose(o, ro[:, qh], atol=1e-12)
         np.testing.assert_allclose(lse, rl[qh], atol=1e-12)
+
+
+@pytest.mark.parametrize("S,R,U,hq,hkv,d", [(64, 4, 2, 4, 2, 16), (96, 6, 3, 6, 3, 8), (64, 4, 4, 8, 4, 8)])
+def test_usp_shares_reassemble_full_attention(S, R, U, hq, hkv, d):
+    """USP: inside groups of U devices an all-to-all trades tokens for heads, and a
+    ring runs across the R/U groups.  Device (head group g, ring rank p) runs the
+    Pass-KV ring of R/U ranks on heads g of the whole sequence; over all devices
+    the shares cover full causal attention exactly once."""
+    q, k, v = _rand((S, hq, d), 21), _rand((S, hkv, d), 22), _rand((S, hkv, d), 23)
+    scale = 1 / math.sqrt(d)
+    ro, rl = _torch_attention(q, k, v, scale, causal=True)
+    P, gq, gk = R // U, hq // U, hkv // U
+    o = np.full((S, hq, d), np.nan)
+    lse = np.full((hq, S), np.nan)
+    for g in range(U):
+        qh, kh = np.arange(g * gq, (g + 1) * gq), np.arange(g * gk, (g + 1) * gk)
+        for p in range(P):
+            pos = oracle.zigzag_positions(S, P, p)
+            blocks = [(k[ps][:, kh], v[ps][:, kh], ps) for ps in (oracle.zigzag_positions(S, P, s) for s in range(P))]
+            oo, ll, _ = oracle.rank_forward(q[pos][:, qh], pos, blocks, None, scale)
+            o[np.ix_(pos, qh)] = oo
+            lse[np.ix_(qh, pos)] = ll
+    np.testing.assert_allclose(o, ro, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, atol=1e-12)
