@@ -232,13 +232,17 @@ def _side_stream(dev):
 class _Feeder:
     """Supplies the block of each step (a tuple of tensors: (K, V) for Pass KV,
     (Q,) for Pass Q), optionally through a double-buffered receive buffer filled
-    on a side stream (the stand-in for the ring transfer)."""
+    on a side stream (the stand-in for the ring transfer).  ``pack`` (optional)
+    groups the source's tensors: each group lands row-wise concatenated in one
+    buffer, e.g. [(0, 2), (1, 3)] turns (K_a, V_a, K_b, V_b) into
+    ([K_a; K_b], [V_a; V_b])."""
 
-    def __init__(self, block_of_source, sched, stage, dev):
+    def __init__(self, block_of_source, sched, stage, dev, pack=None):
         self.block_of_source = block_of_source
         self.sched = sched
         self.stage = stage
         self.dev = dev
+        self.pack = pack
         if stage:
             self.side = _side_stream(dev)
             # The receive buffers come from torch's caching allocator, which may hand
@@ -251,11 +255,16 @@ class _Feeder:
             self.free_recorded = [False, False]
             self._issue(0)
 
+    def _groups(self, src):
+        return [(i,) for i in range(len(src))] if self.pack is None else self.pack
+
     def _issue(self, t):
         src = tuple(self.block_of_source(self.sched[t]))
+        groups = self._groups(src)
         slot = t % 2
         if self.buf[slot] is None:
-            bufs = tuple(torch.empty_like(x) for x in src)
+            bufs = tuple(torch.empty((sum(src[i].shape[0] for i in g), *src[g[0]].shape[1:]), dtype=src[g[0]].dtype,
+                                     device=src[g[0]].device) for g in groups)
             for b in bufs:
                 # written on the side stream: keep the blocks until its work is done
                 b.record_stream(self.side)
@@ -264,13 +273,20 @@ class _Feeder:
         with torch.cuda.stream(self.side):
             if self.free_recorded[slot]:
                 self.side.wait_event(self.free[slot])
-            for b, x in zip(bufs, src):
-                b.copy_(x, non_blocking=True)
+            for b, g in zip(bufs, groups):
+                row = 0
+                for i in g:
+                    n = src[i].shape[0]
+                    b[row:row + n].copy_(src[i], non_blocking=True)
+                    row += n
             self.ready[slot].record(self.side)
 
     def get(self, t, compute):
         if not self.stage:
-            return tuple(self.block_of_source(self.sched[t]))
+            src = tuple(self.block_of_source(self.sched[t]))
+            if self.pack is None:
+                return src
+            return tuple(torch.cat([src[i] for i in g], dim=0) for g in self.pack)
         slot = t % 2
         compute.wait_event(self.ready[slot])
         if t + 1 < len(self.sched):

@@ -149,39 +149,56 @@ class PartialPrefillRank:
         return [cpattn.cp_ring_source(self.R, self.rank, t) for t in range(self.R)]
 
     def problems(self, step: int):
-        """(cached problem, new problem) of one step: every cached key is visible
-        to every new token (FULL); the new tokens follow the causal chunk classes
-        of the Pass KV step."""
+        """The step's calls on the visiting rank's receive buffer, which holds its
+        cached share (rows [0, 2 cc)) and then its new share (rows [2 cc, 2 cc + 2 cn)).
+        Every cached key is visible to every new token (FULL); the new tokens follow
+        the causal chunk classes of the Pass KV step.  Off the diagonal step those
+        classes are FULL or SKIP, so one call covers the step: the cached share as one
+        FULL segment and the visible new chunks as the other (a segment whose pairs are
+        all FULL or SKIP may span several position ranges).  The diagonal step takes
+        two calls."""
         R, cc, cn, P = self.R, self.cc, self.cn, self.P
         s = cpattn.cp_ring_source(R, self.rank, step)
         qa, qb = self._chunks(self.N, self.rank)
         q_seg = [(0, P + qa * cn, cn), (cn, P + qb * cn, cn)]
         ca, cb = self._chunks(P, s)
-        F = cpattn.CP_MASK_FULL
-        cached = cpattn.make_problem(self.hq, self.hkv, self.dim, self.scale, 2 * cn, 2 * cc, q_seg,
-                                     [(0, ca * cc, cc), (cc, cb * cc, cc)], [[F, F], [F, F]])
         na, nb = self._chunks(self.N, s)
-        new = cpattn.make_problem(self.hq, self.hkv, self.dim, self.scale, 2 * cn, 2 * cn, q_seg,
-                                  [(0, P + na * cn, cn), (cn, P + nb * cn, cn)],
-                                  cpattn.cp_step_masks(R, self.rank, step, False))
-        return cached, new
+        F, S_ = cpattn.CP_MASK_FULL, cpattn.CP_MASK_SKIP
+        rows = 2 * cc + 2 * cn
+        mk = lambda kv_seg, masks: cpattn.make_problem(self.hq, self.hkv, self.dim, self.scale, 2 * cn, rows, q_seg,
+                                                        kv_seg, masks)
+        m = cpattn.cp_step_masks(R, self.rank, step, False)  # (query chunk, new chunk) classes
+        new_segs = [(2 * cc, P + na * cn, cn), (2 * cc + cn, P + nb * cn, cn)]
+        cached_one = (0, ca * cc, 2 * cc)  # FULL only: its position is never read
+        if any(c not in (F, S_) for row in m for c in row):
+            return [mk([(0, ca * cc, cc), (cc, cb * cc, cc)], [[F, F], [F, F]]), mk(new_segs, m)]
+        live = [j for j in range(2) if any(m[i][j] != S_ for i in range(2))]
+        if not live:
+            return [mk([cached_one], [[F, S_], [F, S_]])]
+        if len(live) == 1:
+            j = live[0]
+            return [mk([cached_one, new_segs[j]], [[F, m[0][j]], [F, m[1][j]]])]
+        if all(m[i][0] == m[i][1] for i in range(2)):
+            return [mk([cached_one, (2 * cc, P + na * cn, 2 * cn)], [[F, m[0][0]], [F, m[1][0]]])]
+        return [mk([(0, ca * cc, cc), (cc, cb * cc, cc)], [[F, F], [F, F]]), mk(new_segs, m)]
 
     def forward(self, q_new, kv_of_source, stage: bool = True, timer=None):
         """q_new: device bf16 [2*cn, Hq, D]; kv_of_source(s) -> (k_cached, v_cached,
-        k_new, v_new) with [2*cc or 2*cn, Hkv, D].  Returns merged (O, LSE)."""
+        k_new, v_new) with [2*cc or 2*cn, Hkv, D], received into one buffer per
+        tensor kind (cached rows, then new rows).  Returns merged (O, LSE)."""
         rows = 2 * self.cn
         sched = self.schedule()
         check_schedule(self.R, sched)
         compute = torch.cuda.current_stream(self.device)
         o = torch.empty((rows, self.hq, self.dim), dtype=torch.float32, device=self.device)
         lse = torch.empty((self.hq, rows), dtype=torch.float32, device=self.device)
-        feeder = _Feeder(kv_of_source, sched, stage, self.device)
+        feeder = _Feeder(kv_of_source, sched, stage, self.device, pack=[(0, 2), (1, 3)])
         first = True
         for t in range(self.R):
-            kc, vc, kn, vn = feeder.get(t, compute)
+            k, v = feeder.get(t, compute)
             if timer:
                 timer(t, "fwd_begin", compute)
-            for p, k, v in zip(self.problems(t), (kc, kn), (vc, vn)):
+            for p in self.problems(t):
                 if first:  # the query segments cover every row: this call writes them all
                     cpattn.cp_attn_fwd_step(p, q_new, k, v, o, lse, stream=compute)
                     first = False

@@ -78,7 +78,9 @@ typedef struct cp_segment {
  * segments (the source rank's two chunks).  Query segments must not share
  * rows.  mask[i][j] is the class of (query segment i, KV segment j); the
  * kernels trust FULL and SKIP and apply element masks only on partially
- * visible tiles of DIAG_CAUSAL and DOC pairs.
+ * visible tiles of DIAG_CAUSAL and DOC pairs.  Positions are read only for
+ * DIAG_CAUSAL and DOC pairs: a segment whose pairs are all FULL or SKIP may
+ * hold rows from several position ranges (its pos0 is then not used).
  *
  * Sliding window ("Announcing Long-Context Training ...", closing section:
  * models such as Gemma mix sliding-window layers with global ones): with

@@ -36,10 +36,14 @@ def test_partial_prefill_problems_count_the_right_pairs(P, N, R):
         _, new_r = ov.partial_prefill_positions(P, N, R, r)
         for t, s in enumerate(rank.schedule()):
             cached_s, new_s = ov.partial_prefill_positions(P, N, R, s)
-            pc, pn = rank.problems(t)
-            assert cpattn.cp_count_pairs(pc) == int(oracle.visibility(new_r, cached_s).sum())
-            assert cpattn.cp_count_pairs(pn) == int(oracle.visibility(new_r, new_s).sum())
-            total += cpattn.cp_count_pairs(pc) + cpattn.cp_count_pairs(pn)
+            probs = rank.problems(t)
+            # one call per step, two on the diagonal step (where the new share has causal pairs)
+            assert len(probs) == (2 if s == r else 1)
+            got = sum(cpattn.cp_count_pairs(p) for p in probs)
+            assert got == int(oracle.visibility(new_r, cached_s).sum()) + int(oracle.visibility(new_r, new_s).sum())
+            for p in probs:  # every segment lies inside the receive buffer [cached ; new]
+                assert p.kv_rows == len(cached_s) + len(new_s)
+            total += got
     S = P + N
     assert total == int(oracle.visibility(np.arange(P, S), np.arange(S)).sum())
 
