@@ -6,16 +6,18 @@
 //   P = exp(scale q.k - LSE) on visible pairs,  dS = P (dO.v - delta),
 //   dV_j = sum_i P_ij dO_i,  dK_j = scale sum_i dS_ij q_i,  dQ_i += scale sum_j dS_ij k_j.
 //
-// Two kernels, neither with atomics (wave64, 32x32x16 bf16 MFMA, fp32 accumulation):
+// Two kernels, no atomics in their loops (wave64, 32x32x16 bf16 MFMA, fp32 accumulation):
 //  * bwd_dkdv_kernel: a 4-wave workgroup owns 128 keys (32 per wave) of one KV
 //    head, holds their K and V rows in registers, and walks every (query head of
 //    the group, 32-row query tile) that can see them.  Query and dO tiles, with
-//    their LSE and delta rows, stream HBM -> LDS through a four-slot ring three
-//    tiles ahead.  S = Q K^T and dP = dO V^T put the queries on the MFMA M axis,
+//    their LSE and delta rows, stream HBM -> LDS through a four-slot ring two
+//    items ahead.  S = Q K^T and dP = dO V^T put the queries on the MFMA M axis,
 //    so each lane holds one key and its P / dS registers are directly the B
 //    operands of dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T come from the
 //    row-major LDS tiles through the transposing LDS read.  dK/dV stay in
-//    registers and are written once.
+//    registers and are written once; when an unbalanced block's items are split
+//    over several workgroups, each adds its part once at the end (atomic adds,
+//    staged through LDS).
 //  * bwd_dq_kernel: the forward kernel's shape (8 waves, 32 query rows of one
 //    head per wave, heads of a GQA group sharing K/V tiles, four-slot ring of
 //    K/V tiles): S^T = K Q^T and dP^T = V dO^T put one query per lane, so the

@@ -30,8 +30,9 @@
 //  * Tiles with no visible pair are never visited (block-sparse skip); the
 //    element mask runs only on partially visible or ragged tiles.
 //  * Work items are dealt to the XCDs round-robin: each XCD keeps the same head
-//    blocks (K/V shared in its L2), latest query positions first, and query
-//    tiles of a head block shared by several XCDs interleave across them.
+//    blocks (K/V shared in its L2; with Hkv a multiple of 8 all head blocks of
+//    a KV head share one XCD), latest query positions first, and query tiles of
+//    a head block shared by several XCDs interleave across them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>

@@ -10,8 +10,8 @@ them):
   the same counters read for a plain device-to-device copy of known size made
   at the start of the same program (``bench.py --calibrate-copy-mib``), so the
   result is in bytes of memory traffic per launch.  The summary records a
-  SHA-256 of the kernel's source files; ``read_traffic`` returns the figure
-  only while those sources are unchanged.
+  SHA-256 of the kernel's source code (comments and layout ignored);
+  ``read_traffic`` returns the figure only while that code is unchanged.
 * ``counters``: MFMA utilisation and instruction mix per kernel from one
   ``--pmc`` pass over the SQ counters listed in ``SQ_COUNTERS``.
 * ``dispatches``: the individual dispatches of chosen kernels from a
@@ -58,12 +58,21 @@ def _family(kernel: str) -> str:
     raise KeyError(f"no source list for kernel {kernel!r}")
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed: what the
+    compiler sees, so that editing a comment does not mark measurements stale."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(kernel: str) -> str:
+    """SHA-256 over the code (comments and layout ignored) of a kernel's sources."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES[_family(kernel)]:
         h.update(rel.encode())
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()
 
 
