@@ -8,6 +8,7 @@ import re
 
 import numpy as np
 import pytest
+from hypothesis import given, settings, strategies as st
 
 import oracle
 from context_long_attention_amd import cpattn
@@ -349,3 +350,49 @@ def test_kv_split_validation():
         assert e.value.status == cpattn.CP_ERR_INVALID_ARG
     p.kv_split = 8
     assert cpattn.cp_count_pairs(p) == 64 * 64
+
+
+@st.composite
+def _random_problem(draw):
+    """Arbitrary segments (not ring-shaped): 1-2 query and 1-2 KV segments at random
+    positions, DIAG or DOC classes (the ones whose visibility the host derives from
+    positions), optional documents and window."""
+    hq, hkv = draw(st.sampled_from([(8, 2), (4, 4), (6, 2), (16, 1)]))
+    d = draw(st.sampled_from([64, 128]))
+    span = 600
+    def segs(n_max):
+        out, row = [], 0
+        for _ in range(draw(st.integers(1, n_max))):
+            ln = draw(st.integers(0, 200))
+            out.append((row, draw(st.integers(0, span)), ln))
+            row += ln
+        return out, row
+    qs, q_rows = segs(2)
+    ks, kv_rows = segs(2)
+    docs = draw(st.booleans())
+    cu = None
+    if docs:
+        cuts = sorted(set(draw(st.lists(st.integers(1, span + 200), max_size=6))))
+        cu = np.array([0] + cuts + [span + 201], dtype=np.int32)
+    m = cpattn.CP_MASK_DOC if docs else cpattn.CP_MASK_DIAG_CAUSAL
+    window = draw(st.sampled_from([0, 0, 1, 17, 64, 150]))
+    return hq, hkv, d, qs, q_rows, ks, kv_rows, m, cu, window
+
+
+@settings(max_examples=300, deadline=None)
+@given(_random_problem())
+def test_block_map_and_pairs_on_arbitrary_segments(prob):
+    """The host block map and pair count against the oracle's brute force on
+    problems the ring never builds: overlapping position ranges, empty segments,
+    segments that start mid-document."""
+    hq, hkv, d, qs, q_rows, ks, kv_rows, m, cu, window = prob
+    p = cpattn.make_problem(hq, hkv, d, 0.1, max(q_rows, 1), max(kv_rows, 1), qs, ks, [[m, m], [m, m]],
+                            None if cu is None else cu.ctypes.data, 0 if cu is None else len(cu) - 1, window)
+    bm, bn = cpattn.cp_tile_shape(hq, hkv, d)
+    ref = oracle.tile_map([(s[1], s[2]) for s in qs], [(s[1], s[2]) for s in ks], bm, bn, cu, window or None)
+    assert np.array_equal(cpattn.cp_block_map(p), ref)
+    want = 0
+    for _, qp, ql in qs:
+        for _, kp, kl in ks:
+            want += int(oracle.visibility(np.arange(qp, qp + ql), np.arange(kp, kp + kl), cu, window or None).sum())
+    assert cpattn.cp_count_pairs(p) == want
