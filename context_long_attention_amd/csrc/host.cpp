@@ -63,9 +63,10 @@ cp_status validate_problem(const cp_attn_problem* p, bool device_docs) {
     if (p->kv_split < 0 || p->kv_split > kMaxKvSplit)
         return fail(CP_ERR_INVALID_ARG, "kv_split must be in [0, " + std::to_string(kMaxKvSplit) + "]");
     bool any_doc = false;
+    // Range checks written so that no sum of caller values can overflow.
     for (int i = 0; i < p->n_q_seg; ++i) {
         const cp_segment& s = p->q_seg[i];
-        if (s.row0 < 0 || s.len < 0 || s.pos0 < 0 || s.row0 + s.len > p->q_rows || s.pos0 + s.len > kPosLimit)
+        if (s.row0 < 0 || s.len < 0 || s.pos0 < 0 || s.len > p->q_rows - s.row0 || s.pos0 > kPosLimit - s.len)
             return fail(CP_ERR_INVALID_ARG, "query segment out of range");
         for (int j = 0; j < p->n_kv_seg; ++j) {
             int m = p->mask[i][j];
@@ -81,7 +82,7 @@ cp_status validate_problem(const cp_attn_problem* p, bool device_docs) {
     }
     for (int j = 0; j < p->n_kv_seg; ++j) {
         const cp_segment& s = p->kv_seg[j];
-        if (s.row0 < 0 || s.len < 0 || s.pos0 < 0 || s.row0 + s.len > p->kv_rows || s.pos0 + s.len > kPosLimit)
+        if (s.row0 < 0 || s.len < 0 || s.pos0 < 0 || s.len > p->kv_rows - s.row0 || s.pos0 > kPosLimit - s.len)
             return fail(CP_ERR_INVALID_ARG, "KV segment out of range");
     }
     if (p->n_kv_seg == 2) {

@@ -140,6 +140,7 @@ extern "C" cp_status cp_merge_partials(float* o_acc, float* lse_acc, const float
     if (!o_acc || !lse_acc || !o_step || !lse_step) return fail(CP_ERR_INVALID_ARG, "NULL pointer");
     if (!all_aligned16({o_acc, lse_acc, o_step, lse_step}))
         return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+    if (rows > (int64_t(1) << 40) / heads) return fail(CP_ERR_UNSUPPORTED, "too large");  // keeps the product in range
     const int64_t threads = rows * heads * (head_dim / 4);
     const int64_t grid = ceil_div(threads, kThreads);
     if (grid > 0x7fffffff) return fail(CP_ERR_UNSUPPORTED, "too large");
@@ -177,6 +178,7 @@ extern "C" cp_status cp_merge_partials_n(float* o_out, float* lse_out, const flo
     prm.rows = rows;
     prm.heads = heads;
     prm.n = n_parts;
+    if (rows > (int64_t(1) << 40) / heads) return fail(CP_ERR_UNSUPPORTED, "too large");  // keeps the product in range
     const int64_t threads = rows * heads * (head_dim / 4);
     const int64_t grid = ceil_div(threads, kThreads);
     if (grid > 0x7fffffff) return fail(CP_ERR_UNSUPPORTED, "too large");
@@ -196,6 +198,7 @@ extern "C" cp_status cp_attn_bwd_prep(const void* d_o, const float* o, float* de
     if (rows == 0) return CP_OK;
     if (!d_o || !o || !delta) return fail(CP_ERR_INVALID_ARG, "NULL pointer");
     if (!all_aligned16({d_o, o, delta})) return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+    if (rows > (int64_t(1) << 40) / heads) return fail(CP_ERR_UNSUPPORTED, "too large");  // keeps the product in range
     const int64_t threads = rows * heads * (head_dim / 4);
     const int64_t grid = ceil_div(threads, kThreads);
     if (grid > 0x7fffffff) return fail(CP_ERR_UNSUPPORTED, "too large");

@@ -132,6 +132,11 @@ def test_validation_rejects_bad_problems(lib):
     assert status(q_segments=[(0, 0, 65)]) == cpattn.CP_ERR_INVALID_ARG
     assert status(q_segments=[(0, 0, 40), (30, 100, 20)]) == cpattn.CP_ERR_INVALID_ARG
     assert status(kv_segments=[(10, 0, 60)]) == cpattn.CP_ERR_INVALID_ARG
+    big = 1 << 62  # row0 + len and pos0 + len would overflow int64
+    assert status(q_segments=[(big, 0, big)]) == cpattn.CP_ERR_INVALID_ARG
+    assert status(kv_segments=[(0, big, big)]) == cpattn.CP_ERR_INVALID_ARG
+    assert status(q_segments=[(0, (1 << 31) - 64, 64)]) == cpattn.CP_OK
+    assert status(q_segments=[(0, (1 << 31) - 63, 64)]) == cpattn.CP_ERR_INVALID_ARG
     assert status(masks=[[7, F], [F, F]]) == cpattn.CP_ERR_INVALID_ARG
     assert status(masks=[[cpattn.CP_MASK_DOC, F], [F, F]]) == cpattn.CP_ERR_INVALID_ARG  # no cu_seqlens
     assert status(scale=float("inf")) == cpattn.CP_ERR_INVALID_ARG
@@ -149,6 +154,10 @@ def test_validation_rejects_bad_problems(lib):
     assert lib.cp_merge_partials_n(None, None, None, None, 2, 10, 4, 96, None) == cpattn.CP_ERR_UNSUPPORTED
     assert lib.cp_attn_bwd_prep(None, None, None, 10, 4, 72, None) == cpattn.CP_ERR_UNSUPPORTED
     assert b"head_dim" in lib.cp_last_error()
+    # sizes whose element count overflows int64 are refused before any pointer is used
+    huge, addr = 1 << 61, 1 << 20
+    assert lib.cp_merge_partials(addr, addr, addr, addr, huge, 64, 128, None) == cpattn.CP_ERR_UNSUPPORTED
+    assert lib.cp_attn_bwd_prep(addr, addr, addr, huge, 64, 128, None) == cpattn.CP_ERR_UNSUPPORTED
     # misaligned tensor pointers are rejected before any launch (never dereferenced;
     # checked only without a GPU, where a regression could not launch on them)
     import torch
