@@ -148,7 +148,7 @@ class RankRing:
         # steps with no visible pair are neither received nor computed (their
         # partial is the merge identity); step 0 (the diagonal) is always live
         live = [t for t in range(len(sched)) if keep_steps or t == 0 or self.source_live(sched[t])]
-        feeder = _Feeder(kv_of_source, [sched[t] for t in live], stage, dev)
+        feeder = _Feeder(kv_of_source, [sched[t] for t in live], stage, dev, local=self.rank)
         for i, t in enumerate(live):
             src = sched[t]
             k, v = feeder.get(i, compute)
@@ -191,7 +191,7 @@ class RankRing:
         # as in the forward: steps with no visible pair are skipped (their dK/dV
         # are zero; with keep_steps they are returned as zeros)
         live = [t for t in range(len(sched)) if t == 0 or self.source_live(sched[t])]
-        feeder = _Feeder(kv_of_source, [sched[t] for t in live], stage, dev)
+        feeder = _Feeder(kv_of_source, [sched[t] for t in live], stage, dev, local=self.rank)
         dk = dv = None
         for t, src in enumerate(sched):
             if t not in live:
@@ -235,14 +235,17 @@ class _Feeder:
     on a side stream (the stand-in for the ring transfer).  ``pack`` (optional)
     groups the source's tensors: each group lands row-wise concatenated in one
     buffer, e.g. [(0, 2), (1, 3)] turns (K_a, V_a, K_b, V_b) into
-    ([K_a; K_b], [V_a; V_b])."""
+    ([K_a; K_b], [V_a; V_b]).  ``local`` (optional) is the source whose block
+    the device already holds (the rank itself): it is read in place, as a ring
+    reads its own block without a transfer (only without ``pack``)."""
 
-    def __init__(self, block_of_source, sched, stage, dev, pack=None):
+    def __init__(self, block_of_source, sched, stage, dev, pack=None, local=None):
         self.block_of_source = block_of_source
         self.sched = sched
         self.stage = stage
         self.dev = dev
         self.pack = pack
+        self.local = local if pack is None else None
         if stage:
             self.side = _side_stream(dev)
             # The receive buffers come from torch's caching allocator, which may hand
@@ -258,7 +261,12 @@ class _Feeder:
     def _groups(self, src):
         return [(i,) for i in range(len(src))] if self.pack is None else self.pack
 
+    def _in_place(self, t):
+        return self.local is not None and self.sched[t] == self.local
+
     def _issue(self, t):
+        if self._in_place(t):
+            return
         src = tuple(self.block_of_source(self.sched[t]))
         groups = self._groups(src)
         slot = t % 2
@@ -282,7 +290,9 @@ class _Feeder:
             self.ready[slot].record(self.side)
 
     def get(self, t, compute):
-        if not self.stage:
+        if not self.stage or self._in_place(t):
+            if self.stage and t + 1 < len(self.sched):
+                self._issue(t + 1)
             src = tuple(self.block_of_source(self.sched[t]))
             if self.pack is None:
                 return src
@@ -294,7 +304,7 @@ class _Feeder:
         return self.buf[slot]
 
     def release(self, t, compute):
-        if self.stage:
+        if self.stage and not self._in_place(t):
             slot = t % 2
             self.free[slot].record(compute)
             self.free_recorded[slot] = True

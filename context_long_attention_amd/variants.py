@@ -97,7 +97,7 @@ class PassQRank:
         sched = self.schedule()
         check_schedule(self.R, sched)
         compute = torch.cuda.current_stream(self.device)
-        feeder = _Feeder(lambda s: (q_of_source(s),), sched, stage, self.device)
+        feeder = _Feeder(lambda s: (q_of_source(s),), sched, stage, self.device, local=self.rank)
         out = []
         for t, s in enumerate(sched):
             (q,) = feeder.get(t, compute)

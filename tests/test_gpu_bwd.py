@@ -91,6 +91,9 @@ RAGGED = [
     ("aligned_g4_d128", 2 * 2 * 512, 2, 8, 2, 128),
     ("aligned_g1_d64", 2 * 4 * 256, 4, 4, 4, 64),
     ("r16_c256", 2 * 16 * 256, 16, 8, 2, 128),
+    # the Llama-3-8B head shape (Hq=32, Hkv=8) and a group of 8 at D=64
+    ("hkv8_g4_d128", 2 * 2 * 96, 2, 32, 8, 128),
+    ("g8_d64", 2 * 2 * 66, 2, 8, 1, 64),
 ]
 
 
