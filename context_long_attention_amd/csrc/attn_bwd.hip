@@ -769,6 +769,7 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     prm.n_work_q = int32_t(work_q);
     prm.n_hb = p->hq / gq.hpw;
     prm.kv_split = (p->kv_split > 0) ? p->kv_split : dkdv_split(p, nullptr, device_cus());
+    if (work_kv * prm.kv_split > (int64_t(1) << 30)) return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     hipError_t e = hipSuccess;
     if (work_kv > 0 && prm.kv_split > 1) {
         // split workgroups add into dK/dV: clear the rows of both KV segments first
@@ -782,8 +783,6 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
         if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("dK/dV clear launch: ") + hipGetErrorString(e));
     }
     if (work_kv > 0) {
-        if (work_kv * prm.kv_split > (int64_t(1) << 30))
-            return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
         const int grid = int(work_kv * prm.kv_split);
         e = (p->head_dim == 128) ? launch_dkdv<128>(prm, grid, stream) : launch_dkdv<64>(prm, grid, stream);
         if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd dK/dV launch: ") + hipGetErrorString(e));
