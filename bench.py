@@ -171,11 +171,11 @@ def cpu_baseline(w, rank, heads):
 
 
 def fwd_algorithmic_bytes(w, live_rows, merge):
-    """Bytes one forward step launch must move at least: Q, K and V read once
-    (bf16); then for the rows that see a key in the step, O and LSE (fp32)
-    written once, or, when the launch merges into the accumulator, read and
-    written once."""
-    q = w.local * w.hq * w.dim * 2
+    """Bytes one forward step launch must move at least: K and V read once
+    (bf16); then for the rows that see a key in the step, Q read once (bf16)
+    and O and LSE (fp32) written once, or, when the launch merges into the
+    accumulator, read and written once."""
+    q = live_rows * w.hq * w.dim * 2
     kv = 2 * w.local * w.hkv * w.dim * 2
     out = live_rows * w.hq * (w.dim + 1) * 4
     return q + kv + out * (2 if merge else 1)

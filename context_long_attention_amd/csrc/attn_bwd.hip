@@ -496,7 +496,7 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
             u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-            if (row_valid) {
+            if (row_valid && n_it > 0) {
                 a = *reinterpret_cast<const u32x4*>(p.q + off + 16 * ds);
                 b = *reinterpret_cast<const u32x4*>(p.d_o + off + 16 * ds);
             }
@@ -505,7 +505,7 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
         }
     }
     float nl = 0.f, dl = 0.f;
-    if (row_valid) {
+    if (row_valid && n_it > 0) {
         const float l = p.lse[(int64_t)head * p.q_rows + my_row];
         nl = (l == -INFINITY) ? 0.f : -l * kLog2e;  // a row with no visible key is fully masked
         dl = p.delta[(int64_t)head * p.q_rows + my_row];
@@ -736,7 +736,7 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     prm.scale_log2 = p->scale * kLog2e;
     prm.nq_seg = p->n_q_seg;
     prm.nkv_seg = p->n_kv_seg;
-    int64_t nk = 0, nq = 0;
+    int64_t nk = 0;
     for (int i = 0; i < 2; ++i) {
         const bool on = i < p->n_q_seg;
         prm.qs_row0[i] = on ? int32_t(p->q_seg[i].row0) : 0;
@@ -747,16 +747,29 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
         prm.ks_pos0[i] = kon ? int32_t(p->kv_seg[i].pos0) : 0;
         prm.ks_len[i] = kon ? int32_t(p->kv_seg[i].len) : 0;
         nk += ceil_div(prm.ks_len[i], BK);
-        nq += ceil_div(prm.qs_len[i], gq.bm);
     }
     for (int i = 0; i < 2; ++i)
         for (int j = 0; j < 2; ++j)
             prm.mask[i][j] = (i < p->n_q_seg && j < p->n_kv_seg) ? p->mask[i][j] : CP_MASK_SKIP;
     prm.ktiles0 = int32_t(ceil_div(prm.ks_len[0], BK));
     prm.n_ktiles = int32_t(nk);
-    prm.qtiles0 = int32_t(ceil_div(prm.qs_len[0], gq.bm));
-    prm.n_qtiles = int32_t(nq);
     const int64_t work_kv = nk * p->hkv;
+    // dQ: query segments that see no KV segment get nothing and stay out of the
+    // launch (the dK/dV kernel still walks every segment)
+    const cp_attn_problem lq = live_queries(p);
+    BwdParams prm_q = prm;
+    int64_t nq = 0;
+    for (int i = 0; i < 2; ++i) {
+        const bool on = i < lq.n_q_seg;
+        prm_q.qs_row0[i] = on ? int32_t(lq.q_seg[i].row0) : 0;
+        prm_q.qs_pos0[i] = on ? int32_t(lq.q_seg[i].pos0) : 0;
+        prm_q.qs_len[i] = on ? int32_t(lq.q_seg[i].len) : 0;
+        for (int j = 0; j < 2; ++j) prm_q.mask[i][j] = (on && j < p->n_kv_seg) ? lq.mask[i][j] : CP_MASK_SKIP;
+        nq += ceil_div(prm_q.qs_len[i], gq.bm);
+    }
+    prm_q.nq_seg = lq.n_q_seg;
+    prm_q.qtiles0 = int32_t(ceil_div(prm_q.qs_len[0], gq.bm));
+    prm_q.n_qtiles = int32_t(nq);
     const int64_t work_q = nq * (p->hq / gq.hpw);
     if (work_kv == 0 && work_q == 0) return CP_OK;
     if (!q || !k || !v || !d_o || !lse || !delta || !dq_acc || !dk_out || !dv_out)
@@ -766,9 +779,12 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     if (work_kv > (int64_t(1) << 30) || work_q > (int64_t(1) << 30))
         return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     prm.n_work_kv = int32_t(work_kv);
-    prm.n_work_q = int32_t(work_q);
     prm.n_hb = p->hq / gq.hpw;
     prm.kv_split = (p->kv_split > 0) ? p->kv_split : dkdv_split(p, nullptr, device_cus());
+    prm_q.n_work_kv = prm.n_work_kv;
+    prm_q.n_hb = prm.n_hb;
+    prm_q.kv_split = prm.kv_split;
+    prm_q.n_work_q = int32_t(work_q);
     if (work_kv * prm.kv_split > (int64_t(1) << 30)) return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     hipError_t e = hipSuccess;
     if (work_kv > 0 && prm.kv_split > 1) {
@@ -790,11 +806,11 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     if (work_q > 0) {
         const int grid = int(work_q);
         if (p->head_dim == 128)
-            e = (gq.hpw == 4) ? launch_dq<128, 4>(prm, grid, stream)
-                              : (gq.hpw == 2 ? launch_dq<128, 2>(prm, grid, stream) : launch_dq<128, 1>(prm, grid, stream));
+            e = (gq.hpw == 4) ? launch_dq<128, 4>(prm_q, grid, stream)
+                              : (gq.hpw == 2 ? launch_dq<128, 2>(prm_q, grid, stream) : launch_dq<128, 1>(prm_q, grid, stream));
         else
-            e = (gq.hpw == 4) ? launch_dq<64, 4>(prm, grid, stream)
-                              : (gq.hpw == 2 ? launch_dq<64, 2>(prm, grid, stream) : launch_dq<64, 1>(prm, grid, stream));
+            e = (gq.hpw == 4) ? launch_dq<64, 4>(prm_q, grid, stream)
+                              : (gq.hpw == 2 ? launch_dq<64, 2>(prm_q, grid, stream) : launch_dq<64, 1>(prm_q, grid, stream));
         if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd dQ launch: ") + hipGetErrorString(e));
     }
     return CP_OK;

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds) {
             u32x4 val = {0u, 0u, 0u, 0u};
-            if (row_valid) val = *reinterpret_cast<const u32x4*>(qrow + 16 * ds);
+            if (row_valid && n_it > 0) val = *reinterpret_cast<const u32x4*>(qrow + 16 * ds);
             qf[ds] = __builtin_bit_cast(bf16x8, val);
         }
     }
@@ -615,6 +615,11 @@ cp_status fwd_step(const cp_attn_problem* p, const void* q, const void* k, const
                            float* lse_step, uint8_t* tile_map_out, bool merge, hipStream_t stream) {
     cp_status st = validate_problem(p, true);
     if (st != CP_OK) return st;
+    // A merging step leaves rows that see no KV segment untouched: their query
+    // segments stay out of the launch (unless the tile map is asked for, which
+    // covers every query tile).
+    const cp_attn_problem live = (merge && !tile_map_out) ? live_queries(p) : *p;
+    p = &live;
     const TileGeom g = fwd_geom(p->hq, p->hkv);
     FwdParams prm = {};
     prm.q = static_cast<const uint16_t*>(q);

@@ -206,6 +206,25 @@ int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_c
     return 1;
 }
 
+cp_attn_problem live_queries(const cp_attn_problem* p) {
+    cp_attn_problem r = *p;
+    int n = 0;
+    for (int i = 0; i < p->n_q_seg; ++i) {
+        bool live = false;
+        for (int j = 0; j < p->n_kv_seg; ++j) live |= p->mask[i][j] != CP_MASK_SKIP && p->kv_seg[j].len > 0;
+        if (!live || p->q_seg[i].len == 0) continue;
+        r.q_seg[n] = p->q_seg[i];
+        for (int j = 0; j < 2; ++j) r.mask[n][j] = p->mask[i][j];
+        ++n;
+    }
+    for (int i = n; i < 2; ++i) {
+        r.q_seg[i] = cp_segment{0, 0, 0};
+        for (int j = 0; j < 2; ++j) r.mask[i][j] = CP_MASK_SKIP;
+    }
+    r.n_q_seg = n;
+    return r;
+}
+
 TileRange tile_range(int mask, int64_t q0, int64_t q1, int64_t lo0, int64_t kpos0, int64_t klen, int bn) {
     int64_t nkt = ceil_div(klen, bn);
     if (mask == CP_MASK_SKIP || klen == 0 || q1 < q0) return {0, 0};

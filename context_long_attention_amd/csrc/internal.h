@@ -86,4 +86,10 @@ int64_t row_lower_bound(const cp_attn_problem* p, int mask, int64_t q);
 // count.  host_cu: host cu_seqlens for DOC masks; NULL with a DOC mask gives 1.
 int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_cu);
 
+// The problem restricted to its query segments that pair with some KV rows
+// (a mask other than SKIP against a non-empty KV segment), in their order;
+// n_q_seg may become 0.  Rows of the other segments receive nothing in a
+// merging forward step and nothing in dQ, so those launches leave them out.
+cp_attn_problem live_queries(const cp_attn_problem* p);
+
 }  // namespace cpattn

@@ -250,14 +250,16 @@ SQ_COUNTERS = ["SQ_BUSY_CYCLES", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "S
 N_XCD, N_SIMD = 8, 1024  # MI355X: GRBM_GUI_ACTIVE sums the 8 XCDs; 256 CUs x 4 SIMDs
 
 
-def counters(path: str, grid: int | None = None):
+def counters(path: str, grids=None):
     """Per kernel: launches and the per-launch average of every counter in
-    SQ_COUNTERS (only dispatches of `grid` work-items, if given)."""
+    SQ_COUNTERS (only dispatches whose size in work-items is one of `grids`, if
+    given)."""
     per = defaultdict(lambda: defaultdict(float))
     names = {}
+    keep = None if not grids else set(grids)
     with open(path) as f:
         for r in csv.DictReader(f):
-            if grid is not None and int(r["Grid_Size"]) != grid:
+            if keep is not None and int(r["Grid_Size"]) not in keep:
                 continue
             d = int(r["Dispatch_Id"])
             per[d][r["Counter_Name"]] += float(r["Counter_Value"])
@@ -270,8 +272,8 @@ def counters(path: str, grid: int | None = None):
             for k, cs in out.items()}
 
 
-def counters_markdown(path: str, commands, kernels, title: str, grid: int | None = None) -> str:
-    cs = counters(path, grid)
+def counters_markdown(path: str, commands, kernels, title: str, grids=None) -> str:
+    cs = counters(path, grids)
     out = [f"# {title}", "", "Made by:", "", "```", *commands, "```", "",
            "Per launch (average over launches). cycles = GRBM_GUI_ACTIVE / 8 (the counter sums the 8 XCDs);",
            "MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x cycles); VALU/MFMA counts the non-MFMA vector",
@@ -322,7 +324,8 @@ def main(argv=None):
     c.add_argument("--kernel", action="append", required=True)
     c.add_argument("--command", action="append", default=[])
     c.add_argument("--title", default="MFMA utilisation from SQ counters")
-    c.add_argument("--grid", type=int, help="only dispatches of this grid size (work-items)")
+    c.add_argument("--grid", type=int, action="append",
+                   help="only dispatches of this grid size (work-items); may be repeated")
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":

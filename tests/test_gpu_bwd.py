@@ -196,3 +196,58 @@ def test_llama3_8b_fwd_bwd_full_size_sampled():
                                                         vis, w.scale)
         assert_o_close(dk[keys].cpu().numpy(), rdk, f"dK step {t} sampled keys")
         assert_o_close(dv[keys].cpu().numpy(), rdv, f"dV step {t} sampled keys")
+
+
+@pytest.mark.parametrize("masks", ["dead_first", "dead_second", "all_dead"])
+def test_dead_query_segments_left_out(masks):
+    """Query segments that pair only with SKIP are left out of the merging forward
+    launch and of the dQ launch: their rows keep the accumulator and dQ bit for
+    bit, while the live segment (moved to the front when the first is dead) gets
+    the oracle's result, and dK/dV hold only the live rows' terms."""
+    from context_long_attention_amd import cpattn
+    from tests.gpu_common import device_bf16
+    hq, hkv, d, na, nb, m = 8, 2, 128, 64, 96, 128
+    n = na + nb
+    note(f"dead query segments {masks}")
+    q64, q = device_bf16(inputs.chunk_normal(21, 0, n, hq, d))
+    do64, do = device_bf16(inputs.chunk_normal(24, 0, n, hq, d))
+    k64, k = device_bf16(inputs.chunk_normal(22, 0, m, hkv, d))
+    v64, v = device_bf16(inputs.chunk_normal(23, 0, m, hkv, d))
+    F, S_ = cpattn.CP_MASK_FULL, cpattn.CP_MASK_SKIP
+    live_a, live_b = {"dead_first": (False, True), "dead_second": (True, False), "all_dead": (False, False)}[masks]
+    mk = [[F if live_a else S_, S_], [F if live_b else S_, S_]]
+    p = cpattn.make_problem(hq, hkv, d, d ** -0.5, n, m, [(0, 2000, na), (na, 5000, nb)], [(0, 1000, m)], mk)
+    live = np.zeros(n, dtype=bool)
+    live[:na], live[na:] = live_a, live_b
+    vis = np.repeat(live[:, None], m, axis=1)
+    rng = np.random.default_rng(9)
+    # forward: merge into a random valid accumulator
+    o0 = rng.standard_normal((n, hq, d)).astype(np.float32)
+    l0 = (rng.standard_normal((hq, n)) * 3).astype(np.float32)
+    o_acc, l_acc = torch.from_numpy(o0.copy()).cuda(), torch.from_numpy(l0.copy()).cuda()
+    cpattn.cp_attn_fwd_step_merge(p, q, k, v, o_acc, l_acc)
+    ro_t, rl_t = oracle.attention_partial(q64, k64, v64, vis, d ** -0.5)
+    ro, rl = oracle.merge(o0.astype(np.float64), l0.astype(np.float64), ro_t, rl_t)
+    got_o, got_l = o_acc.cpu().numpy(), l_acc.cpu().numpy()
+    assert np.array_equal(got_o[~live], o0[~live]) and np.array_equal(got_l[:, ~live], l0[:, ~live])
+    if live.any():
+        assert_o_close(got_o[live], ro[live], "merged O of the live segment")
+        assert_lse_close(got_l[:, live], rl[:, live], "merged LSE of the live segment")
+    # backward from the step's own LSE (P <= 1) and a small random Delta
+    lse = torch.from_numpy(np.where(np.isfinite(rl_t), rl_t, 0.0).astype(np.float32)).cuda()
+    delta64 = 0.1 * rng.standard_normal((hq, n))
+    delta = torch.from_numpy(delta64.astype(np.float32)).cuda()
+    dq0 = rng.standard_normal((n, hq, d)).astype(np.float32)
+    dq = torch.from_numpy(dq0.copy()).cuda()
+    dk = torch.full((m, hkv, d), 7.0, device="cuda")
+    dv = torch.full((m, hkv, d), 7.0, device="cuda")
+    cpattn.cp_attn_bwd_step(p, q, k, v, do, lse, delta, dq, dk, dv)
+    torch.cuda.synchronize()
+    rdq, rdk, rdv = oracle.attention_backward_partial(q64, k64, v64, do64, lse.cpu().numpy().astype(np.float64),
+                                                      delta.cpu().numpy().astype(np.float64), vis, d ** -0.5)
+    got_dq = dq.cpu().numpy()
+    assert np.array_equal(got_dq[~live], dq0[~live])
+    if live.any():
+        assert_o_close(got_dq[live], dq0[live] + rdq[live], "dQ of the live segment")
+    assert_o_close(dk.cpu().numpy(), rdk, "dK")
+    assert_o_close(dv.cpu().numpy(), rdv, "dV")
