@@ -140,3 +140,62 @@ def test_llama3_8b_packed_fwd_bwd_full_size_sampled(packed, which):
         pos0 = int(p.q_seg[seg].pos0) + (qt - seg * tiles_per_seg) * bm
         ref = oracle.tile_map([(pos0, bm)], kseg, bm, bn, cu)
         assert np.array_equal(got[qt:qt + 1], ref), f"tile map row {qt}"
+
+
+def _periodic_bits(seed, rows, heads, d, period=4099):
+    """bf16 bit patterns of rows that repeat with a prime period, so that no
+    shift by fewer than 4099 whole 64-row tiles maps a tile onto an equal one."""
+    bits = inputs.bf16_bits(inputs.chunk_normal(seed, 0, period, heads, d))
+    return np.tile(bits, ((rows + period - 1) // period, 1, 1))[:rows]
+
+
+@pytest.mark.timeout(900)
+def test_kv_segment_just_under_the_span_limit():
+    """The step kernels' one hard size limit: a KV segment spanning just under
+    1 GiB (524207 rows x Hkv=8 x D=128 bf16, a ragged last tile).  With a
+    256-token window, 16 query rows at the segment's start see its first tile
+    and 16 rows straddling its end see only its last tiles, so every output
+    depends on tiles at the two ends of the span.  Forward O/LSE, dQ and the
+    dK/dV of every visible key against the oracle (which needs only those keys);
+    dK/dV of all other keys exactly zero."""
+    from context_long_attention_amd import cpattn
+    from tests.gpu_common import _to_device, device_bf16
+    hq, hkv, d, n, win = 8, 8, 128, 32, 256
+    m = (1 << 30) // (hkv * d * 2) - 64 - 17
+    assert m * hkv * d * 2 < (1 << 30) and m % 64 == 47
+    note(f"KV span {m * hkv * d * 2} bytes")
+    q64, q = device_bf16(inputs.chunk_normal(31, 0, n, hq, d))
+    do64, do = device_bf16(inputs.chunk_normal(34, 0, n, hq, d))
+    kbits, vbits = _periodic_bits(32, m, hkv, d), _periodic_bits(33, m, hkv, d)
+    k, v = _to_device(kbits), _to_device(vbits)
+    D_ = cpattn.CP_MASK_DIAG_CAUSAL
+    qpos = np.concatenate([np.arange(16), np.arange(m - 8, m + 8)])
+    p = cpattn.make_problem(hq, hkv, d, d ** -0.5, n, m, [(0, 0, 16), (16, m - 8, 16)], [(0, 0, m)],
+                            [[D_, D_], [D_, D_]], window=win)
+    o = torch.empty((n, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    cpattn.cp_attn_fwd_step(p, q, k, v, o, lse)
+    delta = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    cpattn.cp_attn_bwd_prep(do, o, delta, n, hq, d)
+    dq = torch.zeros((n, hq, d), dtype=torch.float32, device="cuda")
+    dk = torch.full((m, hkv, d), 7.0, dtype=torch.float32, device="cuda")
+    dv = torch.full((m, hkv, d), 7.0, dtype=torch.float32, device="cuda")
+    cpattn.cp_attn_bwd_step(p, q, k, v, do, lse, delta, dq, dk, dv)
+    torch.cuda.synchronize()
+    # keys no row sees add nothing: the oracle takes only the visible ones
+    keys = np.concatenate([np.arange(16), np.arange(m - 8 - win + 1, m)])
+    vis = oracle.visibility(qpos, keys, None, win)
+    assert vis[:, :16].any() and vis[:, 16:].any() and vis.any(axis=0).all()
+    k64, v64 = widen(kbits[keys]), widen(vbits[keys])
+    ro, rl = oracle.attention_partial(q64, k64, v64, vis, d ** -0.5)
+    assert_o_close(o.cpu().numpy(), ro, "O at both ends of a 1 GiB KV span")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE at both ends of a 1 GiB KV span")
+    rdq, rdk, rdv = oracle.attention_backward_partial(q64, k64, v64, do64, rl, oracle.delta_rows(do64, ro), vis,
+                                                      d ** -0.5)
+    assert_o_close(dq.cpu().numpy(), rdq, "dQ at both ends of a 1 GiB KV span")
+    keys_dev = torch.from_numpy(keys).cuda()
+    assert_o_close(dk.index_select(0, keys_dev).cpu().numpy(), rdk, "dK of the visible keys")
+    assert_o_close(dv.index_select(0, keys_dev).cpu().numpy(), rdv, "dV of the visible keys")
+    rest = torch.ones(m, dtype=torch.bool, device="cuda")
+    rest[keys_dev] = False
+    assert torch.count_nonzero(dk[rest]).item() == 0 and torch.count_nonzero(dv[rest]).item() == 0
