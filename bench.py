@@ -3,8 +3,8 @@
 A step is one pass of the whole hot path for one rank: the zigzag partition and
 block classes (host), then every ring step's forward kernel with the merge of
 its partial output (step 0 writes the accumulator, later steps merge into it
-inside the kernel), with each visiting KV block staged through a receive buffer
-on a side stream.  Default workload: Llama-3-8B attention shape
+inside the kernel); step 0 reads the rank's own KV block in place and every
+later visiting block is staged through a receive buffer on a side stream.  Default workload: Llama-3-8B attention shape
 (Hq=32, Hkv=8, D=128, bf16) on rank 0's share of S=128K at CP=8 (local 16K
 tokens as two zigzag 8K chunks, 8 ring steps).  Inputs are seeded synthetic
 N(0,1) values rounded to bf16, resident in HBM before timing starts.
