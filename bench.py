@@ -85,15 +85,18 @@ class KernelTimer:
 
 
 def probe_clock(torch, one_step):
-    """Shader clock the forward step kernel runs at, from its own counters: one
-    extra (untimed) pass with cp_debug_clock_probe on; per workgroup of the pass's
-    last launch, clock = cycle-counter difference / 100 MHz tick difference.
+    """Shader clock the forward step kernel runs at, from its own counters: two
+    extra (untimed) passes with cp_debug_clock_probe on (launches after an idle
+    GPU start up to 25% slower and settle within about ten milliseconds, so the
+    first pass only warms up); per workgroup of the last launch, clock =
+    cycle-counter difference / 100 MHz tick difference.
     Workgroups shorter than 10 us (steps where their tile sees no key) are left
     out.  Returns the median over workgroups and per XCD (workgroup id mod 8)."""
     from context_long_attention_amd import cpattn
     buf = torch.zeros(4 * 65536, dtype=torch.int64, device="cuda")
     cpattn.cp_debug_clock_probe(buf)
     try:
+        one_step()
         one_step()
         torch.cuda.synchronize()
     finally:
@@ -112,7 +115,7 @@ def probe_clock(torch, one_step):
                                  for x in range(8)],
             "workgroups": int(keep.sum()),
             "source": "forward step kernel's own cycle / 100 MHz counters (cp_debug_clock_probe), last launch "
-                      "of an extra untimed pass"}
+                      "of two extra untimed passes"}
 
 
 def gemm_reference(torch, n=16384, reps=10):
