@@ -230,6 +230,18 @@ def test_dead_query_segments_left_out(masks):
     ro, rl = oracle.merge(o0.astype(np.float64), l0.astype(np.float64), ro_t, rl_t)
     got_o, got_l = o_acc.cpu().numpy(), l_acc.cpu().numpy()
     assert np.array_equal(got_o[~live], o0[~live]) and np.array_equal(got_l[:, ~live], l0[:, ~live])
+    # asking for the tile map launches every query tile: same results bit for bit, and the map
+    nq, nk = cpattn.cp_block_map_size(p)
+    tm = torch.full((nq, nk), 255, dtype=torch.uint8, device="cuda")
+    o_map, l_map = torch.from_numpy(o0.copy()).cuda(), torch.from_numpy(l0.copy()).cuda()
+    cpattn.cp_attn_fwd_step_merge(p, q, k, v, o_map, l_map, tile_map=tm)
+    assert np.array_equal(o_map.cpu().numpy(), got_o) and np.array_equal(l_map.cpu().numpy(), got_l)
+    bm, bn = cpattn.cp_tile_shape(hq, hkv, d)
+    ref_map = np.concatenate([oracle.tile_map([(2000, na)], [(1000, m)], bm, bn) if live_a else
+                              np.zeros((-(-na // bm), nk), dtype=np.uint8),
+                              oracle.tile_map([(5000, nb)], [(1000, m)], bm, bn) if live_b else
+                              np.zeros((-(-nb // bm), nk), dtype=np.uint8)])
+    assert np.array_equal(tm.cpu().numpy(), ref_map)
     if live.any():
         assert_o_close(got_o[live], ro[live], "merged O of the live segment")
         assert_lse_close(got_l[:, live], rl[:, live], "merged LSE of the live segment")
