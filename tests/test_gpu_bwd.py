@@ -263,3 +263,23 @@ def test_dead_query_segments_left_out(masks):
         assert_o_close(got_dq[live], dq0[live] + rdq[live], "dQ of the live segment")
     assert_o_close(dk.cpu().numpy(), rdk, "dK")
     assert_o_close(dv.cpu().numpy(), rdv, "dV")
+
+
+def test_ring_is_deterministic():
+    """Two runs of the same forward and backward ring give bit-identical O, LSE,
+    dQ and per-step dK/dV (no atomics without the dK/dV split, which is forced
+    off here; with it, only the last bits of dK/dV may vary)."""
+    from context_long_attention_amd.ring import RankRing
+    w = inputs.Workload("det", 2 * 4 * 96, 4, 8, 2, 128, backward=True)
+    inp = RankInputs(w, 1, want_do=True)
+    runs = []
+    for _ in range(2):
+        ring = RankRing(w, 1)
+        ring.kv_split = lambda src: 1
+        o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
+        dq, steps = ring.backward(inp.q, inp.do, o, lse, inp.kv_of_source)
+        torch.cuda.synchronize()
+        runs.append([o.cpu().numpy(), lse.cpu().numpy(), dq.cpu().numpy()]
+                    + [x.cpu().numpy() for _, dk, dv in steps for x in (dk, dv)])
+    for a, b in zip(*runs):
+        assert np.array_equal(a, b)
