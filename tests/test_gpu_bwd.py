@@ -283,3 +283,38 @@ def test_ring_is_deterministic():
                     + [x.cpu().numpy() for _, dk, dv in steps for x in (dk, dv)])
     for a, b in zip(*runs):
         assert np.array_equal(a, b)
+
+
+def test_max_query_heads():
+    """Hq = 8192 (the largest the library accepts), Hkv = 2048: head indices,
+    head blocks and the per-head strides at their limits, with ragged causal
+    tiles; forward O/LSE and dQ/dK/dV against the oracle."""
+    from context_long_attention_amd import cpattn
+    from tests.gpu_common import device_bf16
+    hq, hkv, d, n, m = 8192, 2048, 64, 100, 130
+    note("max query heads")
+    q64, q = device_bf16(inputs.chunk_normal(41, 0, n, hq, d))
+    do64, do = device_bf16(inputs.chunk_normal(44, 0, n, hq, d))
+    k64, k = device_bf16(inputs.chunk_normal(42, 0, m, hkv, d))
+    v64, v = device_bf16(inputs.chunk_normal(43, 0, m, hkv, d))
+    D_ = cpattn.CP_MASK_DIAG_CAUSAL
+    p = cpattn.make_problem(hq, hkv, d, d ** -0.5, n, m, [(0, 30, n)], [(0, 0, m)], [[D_, D_], [D_, D_]])
+    o = torch.empty((n, hq, d), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    cpattn.cp_attn_fwd_step(p, q, k, v, o, lse)
+    delta = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    cpattn.cp_attn_bwd_prep(do, o, delta, n, hq, d)
+    dq = torch.zeros((n, hq, d), dtype=torch.float32, device="cuda")
+    dk = torch.empty((m, hkv, d), dtype=torch.float32, device="cuda")
+    dv = torch.empty((m, hkv, d), dtype=torch.float32, device="cuda")
+    cpattn.cp_attn_bwd_step(p, q, k, v, do, lse, delta, dq, dk, dv)
+    torch.cuda.synchronize()
+    vis = oracle.visibility(np.arange(30, 30 + n), np.arange(m))
+    ro, rl = oracle.attention_partial(q64, k64, v64, vis, d ** -0.5)
+    assert_o_close(o.cpu().numpy(), ro, "O at Hq = 8192")
+    assert_lse_close(lse.cpu().numpy(), rl, "LSE at Hq = 8192")
+    rdq, rdk, rdv = oracle.attention_backward_partial(q64, k64, v64, do64, rl, oracle.delta_rows(do64, ro), vis,
+                                                      d ** -0.5)
+    assert_o_close(dq.cpu().numpy(), rdq, "dQ at Hq = 8192")
+    assert_o_close(dk.cpu().numpy(), rdk, "dK at Hq = 8192")
+    assert_o_close(dv.cpu().numpy(), rdv, "dV at Hq = 8192")
