@@ -104,7 +104,11 @@ def kernel_stats(path: str):
     return rows
 
 
-def stats_markdown(path: str, commands, top: int = 12, title: str | None = None) -> str:
+def stats_markdown(path: str, commands, top: int = 12, title: str | None = None, trace: str | None = None,
+                   timed=()) -> str:
+    """``timed``: (kernel, skip_first, skip_last) triples; with the run's
+    ``--kernel-trace`` CSV (``trace``), each adds the kernel's average over its
+    launches without the first and last ones given (the untimed passes)."""
     rows = kernel_stats(path)
     out = [f"# {title or 'Kernel trace summary'}", "", "Made by:", ""]
     out += ["```", *commands, "```", ""]
@@ -112,6 +116,13 @@ def stats_markdown(path: str, commands, top: int = 12, title: str | None = None)
     for r in rows[:top]:
         out.append(f"| `{r['name']}` | {r['calls']} | {r['total_ms']:.3f} | {r['avg_ms']:.4f} | {r['min_ms']:.4f} | "
                    f"{r['max_ms']:.4f} | {r['pct']:.2f} |")
+    for kernel, first, last in timed:
+        ms = [d[3] for d in dispatch_rows(trace, [kernel]) if d[1] == kernel]
+        sel = ms[first:len(ms) - last]
+        if not sel:
+            raise SystemExit(f"no launches of {kernel!r} left after skipping {first} + {last}")
+        out += ["", f"`{kernel}` over the launches of the timed passes only (launches {first + 1}–{len(ms) - last} "
+                    f"of {len(ms)}): average {sum(sel) / len(sel):.4f} ms."]
     return "\n".join(out) + "\n"
 
 
@@ -300,6 +311,9 @@ def main(argv=None):
     s.add_argument("--command", action="append", default=[])
     s.add_argument("--title")
     s.add_argument("--top", type=int, default=12)
+    s.add_argument("--trace", help="the run's *_kernel_trace.csv (for --timed)")
+    s.add_argument("--timed", action="append", default=[],
+                   help="KERNEL:SKIP_FIRST:SKIP_LAST: also average KERNEL over its launches without the first and last ones")
     s.add_argument("--out", required=True)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch", required=True)
@@ -329,7 +343,13 @@ def main(argv=None):
     c.add_argument("--out", required=True)
     a = ap.parse_args(argv)
     if a.cmd == "stats":
-        text = stats_markdown(a.csv, a.command, a.top, a.title)
+        timed = []
+        for spec in a.timed:
+            kernel, first, last = spec.rsplit(":", 2)
+            timed.append((kernel, int(first), int(last)))
+        if timed and not a.trace:
+            raise SystemExit("--timed needs --trace")
+        text = stats_markdown(a.csv, a.command, a.top, a.title, a.trace, timed)
     elif a.cmd == "dispatches":
         text = dispatches_markdown(a.csv, a.command, a.match, a.last, a.title)
     elif a.cmd == "counters":
