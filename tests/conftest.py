@@ -11,3 +11,10 @@ if ROOT not in sys.path:
 def pytest_configure(config):
     config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU and the built HIP library")
     config.addinivalue_line("markers", "slow: long-running CPU test")
+
+
+def pytest_sessionfinish(session, exitstatus):
+    # the whole-tensor references' worker pool, if a test started it
+    mod = sys.modules.get("tests.oracle_par")
+    if mod is not None:
+        mod.shutdown()

@@ -137,3 +137,55 @@ def sampled_rows(local: int, c: int, n_extra: int, seed: int) -> np.ndarray:
     rng = np.random.default_rng(seed)
     edge = [0, 1, 2, c - 1, c, c + 1, local - 2, local - 1]
     return np.unique(np.concatenate([edge, rng.integers(0, local, n_extra)]))
+
+
+class GroupReference:
+    """Whole-tensor float64 oracle results of one rank for the query heads
+    ``heads`` (whole GQA groups), started in the background at construction so
+    that the GPU ring can run meanwhile.  The backward, when asked for, starts
+    from the oracle's own final O and LSE of every local row (never from GPU
+    output).  Use as a context manager: the shared input files are removed on
+    exit."""
+
+    def __init__(self, inp: RankInputs, order, heads, cu=None, window=0, backward=False):
+        from tests import oracle_par
+        self._par = oracle_par
+        self.order = [int(s) for s in order]
+        self.heads = [int(h) for h in heads]
+        kv = {s: inp.kv_bits[s] for s in self.order}
+        kpos = {s: inp.kpos[s] for s in self.order}
+        self.sh = oracle_par.Shared(inp.q_bits, inp.qpos, kv, kpos, inp.w.scale, cu, window,
+                                    do_bits=inp.do_bits if backward else None)
+        self._fwd = oracle_par.Forward(self.sh, self.heads, self.order)
+        self._fwd_res = None
+        self._bwd_res = None
+
+    def forward(self):
+        """(O [rows, len(heads), D], LSE [len(heads), rows]) in float64."""
+        if self._fwd_res is None:
+            o, lse, _ = self._fwd.result()
+            self._fwd_res = (o, lse)
+        return self._fwd_res
+
+    def backward(self):
+        """(dQ [rows, len(heads), D], per-step list of {kv head: (dK [m, D], dV [m, D])})."""
+        if self._bwd_res is None:
+            o, lse = self.forward()
+            dq, per_step, _ = self._par.Backward(self.sh, self.heads, self.order, o, lse).result()
+            self._bwd_res = (dq, per_step)
+        return self._bwd_res
+
+    def close(self):
+        self.sh.close()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def gqa_heads(kv_head: int, hq: int, hkv: int) -> list[int]:
+    """The query heads that read KV head ``kv_head``."""
+    g = hq // hkv
+    return list(range(kv_head * g, (kv_head + 1) * g))

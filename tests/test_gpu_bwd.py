@@ -5,7 +5,7 @@ import pytest
 
 import oracle
 from context_long_attention_amd import inputs
-from tests.gpu_common import RankInputs, assert_lse_close, assert_o_close, note
+from tests.gpu_common import RankInputs, assert_lse_close, assert_o_close, note, widen
 
 pytestmark = pytest.mark.gpu
 
@@ -168,34 +168,47 @@ def test_dkdv_split_matches_oracle(name, S, R, hq, hkv, d, window, packed, rank)
 
 
 @pytest.mark.timeout(600)
-def test_llama3_8b_fwd_bwd_full_size_sampled():
+def test_llama3_8b_fwd_bwd_full_size():
     """Llama-3-8B shape, rank 0's share of S=256K at CP=16 (local 16K), 16 ring steps
-    forward and backward on the GPU; dQ on sampled rows and each step's dK/dV on
-    sampled keys against the oracle (which sees every row and key they depend on)."""
+    forward and backward on the GPU.  For the query heads of KV head 5 (a whole GQA
+    group) every local row's O, LSE and dQ and every step's dK/dV of every key of
+    the visiting block, against the float64 oracle, whose backward starts from its
+    own O and LSE.  For all 32 heads, sampled rows of O, LSE and dQ."""
+    from tests.gpu_common import GroupReference, gqa_heads
     w = inputs.WORKLOADS["llama3_8b_fwdbwd"]
-    rank = 0
-    inp, ring, o, lse, dq, per_step = _run(w, rank)
+    rank, kvh = 0, 5
+    heads = gqa_heads(kvh, w.hq, w.hkv)
+    from context_long_attention_amd.ring import RankRing
+    note(f"bwd {w.name} full size rank={rank} whole group of KV head {kvh}")
+    inp = RankInputs(w, rank, want_do=True)
+    ring = RankRing(w, rank)
+    sched = ring.schedule()
+    with GroupReference(inp, sched, heads, backward=True) as ref:
+        o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
+        dq, per_step = ring.backward(inp.q, inp.do, o, lse, inp.kv_of_source)
+        torch.cuda.synchronize()
+        h0, h1 = heads[0], heads[-1] + 1
+        ro, rl = ref.forward()
+        assert_o_close(o[:, h0:h1].cpu().numpy(), ro, f"O heads {h0}..{h1 - 1}, all rows")
+        assert_lse_close(lse[h0:h1].cpu().numpy(), rl, f"LSE heads {h0}..{h1 - 1}, all rows")
+        rdq, rsteps = ref.backward()
+        assert_o_close(dq[:, h0:h1].cpu().numpy(), rdq, f"dQ heads {h0}..{h1 - 1}, all rows")
+        for t, (src, dk, dv) in enumerate(per_step):
+            assert src == sched[t]
+            rdk, rdv = rsteps[t][kvh]
+            assert_o_close(dk[:, kvh].cpu().numpy(), rdk, f"dK KV head {kvh} step {t}, all keys")
+            assert_o_close(dv[:, kvh].cpu().numpy(), rdv, f"dV KV head {kvh} step {t}, all keys")
+    # every head on sampled rows (the oracle sees every key they depend on)
     rng = np.random.default_rng(11)
     c, L = w.chunk, w.local
     rows = np.unique(np.concatenate([[0, 1, c - 1, c, c + 1, L - 1], rng.integers(0, L, 20)]))
-    blocks = [inp.kv64[s] for s in ring.schedule()]
-    ro, rl, _ = oracle.rank_forward(inp.q64, inp.qpos, blocks, None, w.scale, rows=rows)
+    blocks = [inp.kv64[s] for s in sched]
+    q_rows, do_rows = widen(inp.q_bits[rows]), widen(inp.do_bits[rows])
+    ro, rl, _ = oracle.rank_forward(q_rows, inp.qpos[rows], blocks, None, w.scale)
     assert_o_close(o[rows].cpu().numpy(), ro, "O sampled rows")
     assert_lse_close(lse[:, rows].cpu().numpy(), rl, "LSE sampled rows")
-    rdq, _, _ = oracle.rank_backward(inp.q64[rows], inp.qpos[rows], inp.do64[rows], ro, rl, blocks, None, w.scale)
+    rdq, _, _ = oracle.rank_backward(q_rows, inp.qpos[rows], do_rows, ro, rl, blocks, None, w.scale)
     assert_o_close(dq[rows].cpu().numpy(), rdq, "dQ sampled rows")
-    # dK/dV of sampled keys need every local row's LSE and delta: take them from the GPU forward
-    lse64 = lse.cpu().numpy().astype(np.float64)
-    delta64 = oracle.delta_rows(inp.do64, o.cpu().numpy())
-    keys = np.unique(np.concatenate([[0, 1, c - 1, c, L - 1], rng.integers(0, L, 12)]))
-    for t in (0, 1, w.cp - 1):
-        src, dk, dv = per_step[t]
-        k64, v64, kpos = inp.kv64[src]
-        vis = oracle.visibility(inp.qpos, kpos[keys])
-        _, rdk, rdv = oracle.attention_backward_partial(inp.q64, k64[keys], v64[keys], inp.do64, lse64, delta64,
-                                                        vis, w.scale)
-        assert_o_close(dk[keys].cpu().numpy(), rdk, f"dK step {t} sampled keys")
-        assert_o_close(dv[keys].cpu().numpy(), rdv, f"dV step {t} sampled keys")
 
 
 @pytest.mark.parametrize("masks", ["dead_first", "dead_second", "all_dead"])

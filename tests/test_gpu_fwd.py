@@ -296,19 +296,24 @@ def _sampled_rows(local, c, n_extra, seed):
     return np.unique(np.concatenate([edge, rng.integers(0, local, n_extra)]))
 
 
-@pytest.mark.timeout(400)
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("rank", [0, 7])
-def test_llama3_8b_forward_full_size_sampled(rank):
-    """Llama-3-8B shape, one rank's share of S=128K at CP=8: the whole ring on the GPU,
-    compared on sampled rows (all heads, every key) with the oracle."""
+def test_llama3_8b_forward_whole_tensor(rank):
+    """Llama-3-8B shape, one rank's share of S=128K at CP=8 (local 16K as two zigzag
+    8K chunks, 8 ring steps of 16K-token KV blocks), run as the bench runs it (fused
+    merge, staged receive buffers): O and LSE of every local row and every one of the
+    32 query heads against the float64 oracle.  Rank 0 holds the first and last
+    chunks (half its rows see nothing after step 0); rank 7 the two middle ones."""
+    from tests.gpu_common import GroupReference
     w = inputs.WORKLOADS["llama3_8b_fwd"]
-    note(f"fwd {w.name} full size rank={rank}")
+    note(f"fwd {w.name} full size rank={rank} whole tensor")
     inp = RankInputs(w, rank)
     ring = _ring(w, rank)
-    o, lse, _ = ring.forward(inp.q, inp.kv_of_source, stage=True)
-    torch.cuda.synchronize()
-    rows = _sampled_rows(w.local, w.chunk, 40, rank)
-    ro, rl, _ = oracle.rank_forward(inp.q64, inp.qpos, _oracle_blocks(inp, ring), None, w.scale, rows=rows)
-    assert_o_close(o[rows].cpu().numpy(), ro, f"O rank {rank}")
-    assert_lse_close(lse[:, rows].cpu().numpy(), rl, f"LSE rank {rank}")
-    assert not torch.isnan(o).any().item()
+    with GroupReference(inp, ring.schedule(), range(w.hq)) as ref:
+        o, lse, _ = ring.forward(inp.q, inp.kv_of_source, stage=True)
+        torch.cuda.synchronize()
+        got_o, got_l = o.cpu().numpy(), lse.cpu().numpy()
+        del o, lse
+        ro, rl = ref.forward()
+    assert_o_close(got_o, ro, f"O rank {rank}, all rows and heads")
+    assert_lse_close(got_l, rl, f"LSE rank {rank}, all rows and heads")

@@ -144,22 +144,40 @@ def test_window_with_packed_documents():
 
 @pytest.mark.timeout(900)
 @pytest.mark.parametrize("rank", [0, 3, 7])
-def test_llama3_8b_window4k_full_size_sampled(rank):
+def test_llama3_8b_window4k_full_size(rank):
     """Hq=32, Hkv=8, D=128, a 4K window over S=128K at CP=8 (local 16K): only the
-    rank's own and its neighbours' blocks are live; forward and backward on sampled
-    rows and keys."""
+    rank's own and its neighbours' blocks are live.  For one whole GQA group (KV head
+    rank mod 8) every local row's O, LSE and dQ and every live step's dK/dV of every
+    key against the float64 oracle, whose backward starts from its own O and LSE;
+    for all heads, sampled rows of O, LSE and dQ."""
     from context_long_attention_amd.ring import RankRing
+    from tests.gpu_common import GroupReference, gqa_heads
     w = inputs.WORKLOADS["llama3_8b_window4k"]
     ring = RankRing(w, rank)
     sched = ring.schedule()
     live = [t for t in range(w.cp) if ring.source_live(sched[t])]
     expect = {0} | ({1} if rank > 0 else set()) | ({w.cp - 1} if rank < w.cp - 1 else set())
     assert set(live) == expect
-    note(f"window {w.name} full size rank={rank} live steps={live}")
+    kvh = rank % w.hkv
+    heads = gqa_heads(kvh, w.hq, w.hkv)
+    h0, h1 = heads[0], heads[-1] + 1
+    note(f"window {w.name} full size rank={rank} live steps={live} whole group of KV head {kvh}")
     inp = RankInputs(w, rank, sources=sorted({sched[t] for t in live}), want_do=True)
-    o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
-    dq, per_step = ring.backward(inp.q, inp.do, o, lse, inp.kv_of_source)
-    torch.cuda.synchronize()
+    with GroupReference(inp, [sched[t] for t in live], heads, window=w.window, backward=True) as ref:
+        o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
+        dq, per_step = ring.backward(inp.q, inp.do, o, lse, inp.kv_of_source)
+        torch.cuda.synchronize()
+        ro, rl = ref.forward()
+        assert_o_close(o[:, h0:h1].cpu().numpy(), ro, f"window O heads {h0}..{h1 - 1}")
+        assert_lse_close(lse[h0:h1].cpu().numpy(), rl, f"window LSE heads {h0}..{h1 - 1}")
+        rdq, rsteps = ref.backward()
+        assert_o_close(dq[:, h0:h1].cpu().numpy(), rdq, f"window dQ heads {h0}..{h1 - 1}")
+        for i, t in enumerate(live):
+            src, dk, dv = per_step[t]
+            assert src == sched[t]
+            rdk, rdv = rsteps[i][kvh]
+            assert_o_close(dk[:, kvh].cpu().numpy(), rdk, f"window dK KV head {kvh} step {t}")
+            assert_o_close(dv[:, kvh].cpu().numpy(), rdv, f"window dV KV head {kvh} step {t}")
     rows = sampled_rows(w.local, w.chunk, 24, rank + 11)
     q_rows, do_rows = widen(inp.q_bits[rows]), widen(inp.do_bits[rows])
     blocks = lambda: inp.blocks([sched[t] for t in live])
@@ -169,19 +187,6 @@ def test_llama3_8b_window4k_full_size_sampled(rank):
     rdq, _, _ = oracle.rank_backward(q_rows, inp.qpos[rows], do_rows, ro, rl, blocks(), None, w.scale,
                                      window=w.window)
     assert_o_close(dq[rows].cpu().numpy(), rdq, "window dQ")
-    lse64 = lse.cpu().numpy().astype(np.float64)
-    delta64 = oracle.delta_rows(inp.do64, o.cpu().numpy())
-    rng = np.random.default_rng(rank)
-    q64, do64 = inp.q64, inp.do64
-    for t in live:
-        src, dk, dv = per_step[t]
-        k64, v64, kpos = inp.kv64[src]
-        keys = np.unique(np.concatenate([[0, w.chunk - 1, w.chunk, w.local - 1], rng.integers(0, w.local, 10)]))
-        vis = oracle.visibility(inp.qpos, kpos[keys], None, w.window)
-        _, rdk, rdv = oracle.attention_backward_partial(q64, k64[keys], v64[keys], do64, lse64, delta64, vis,
-                                                        w.scale)
-        assert_o_close(dk[keys].cpu().numpy(), rdk, f"window dK step {t}")
-        assert_o_close(dv[keys].cpu().numpy(), rdv, f"window dV step {t}")
     for t in range(w.cp):
         if t not in live:
             _, dk, dv = per_step[t]
