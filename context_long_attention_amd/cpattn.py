@@ -20,12 +20,13 @@ CP_OK, CP_ERR_INVALID_ARG, CP_ERR_UNSUPPORTED, CP_ERR_HIP = 0, -1, -2, -3
 CP_MASK_FULL, CP_MASK_DIAG_CAUSAL, CP_MASK_DOC, CP_MASK_SKIP = 0, 1, 2, 3
 CP_TILE_SKIP, CP_TILE_PARTIAL, CP_TILE_FULL = 0, 1, 2
 
-# Every symbol include/cpattn.h declares.
+# Every symbol include/*.h declares (cpattn.h, and cpattn_diag.h for the clock probe).
 EXPORTS = (
     "cp_abi_version", "cp_status_string", "cp_last_error", "cp_partition_zigzag", "cp_ring_source",
     "cp_step_masks", "cp_step_masks_window", "cp_tile_shape", "cp_block_map_size", "cp_block_map",
-    "cp_count_pairs", "cp_bwd_kv_split", "cp_merge_partials_n", "cp_attn_fwd_step", "cp_merge_partials",
-    "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step", "cp_debug_clock_probe",
+    "cp_count_pairs", "cp_bwd_kv_split", "cp_bwd_workspace_size", "cp_merge_partials_n", "cp_attn_fwd_step",
+    "cp_merge_partials", "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step",
+    "cp_debug_clock_probe",
 )
 
 
@@ -79,13 +80,14 @@ def lib():
             "cp_block_map": ([P, vp], i32),
             "cp_count_pairs": ([P, vp], i32),
             "cp_bwd_kv_split": ([P, i32, vp], i32),
+            "cp_bwd_workspace_size": ([P, i32, vp], i32),
             "cp_attn_fwd_step": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
             "cp_merge_partials": ([f32p, f32p, f32p, f32p, i64, i32, i32, vp], i32),
             "cp_merge_partials_n": ([f32p, f32p, vp, vp, i32, i64, i32, i32, vp], i32),
             "cp_attn_fwd_step_merge": ([P, vp, vp, vp, f32p, f32p, vp, vp], i32),
             "cp_debug_clock_probe": ([vp, i64], i32),
             "cp_attn_bwd_prep": ([vp, f32p, f32p, i64, i32, i32, vp], i32),
-            "cp_attn_bwd_step": ([P, vp, vp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp], i32),
+            "cp_attn_bwd_step": ([P, vp, vp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp, i64, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -198,6 +200,13 @@ def cp_bwd_kv_split(p: cp_attn_problem, n_cu: int) -> int:
     return out.value
 
 
+def cp_bwd_workspace_size(p: cp_attn_problem, kv_split: int) -> int:
+    """Workspace bytes cp_attn_bwd_step needs for the dK/dV split kv_split."""
+    out = ctypes.c_int64()
+    _check(lib().cp_bwd_workspace_size(ctypes.byref(p), kv_split, ctypes.byref(out)))
+    return out.value
+
+
 def cp_count_pairs(p: cp_attn_problem) -> int:
     out = ctypes.c_int64()
     _check(lib().cp_count_pairs(ctypes.byref(p), ctypes.byref(out)))
@@ -240,6 +249,10 @@ def cp_attn_bwd_prep(d_o, o, delta, rows, heads, head_dim, stream=None):
     _check(lib().cp_attn_bwd_prep(_ptr(d_o), _ptr(o), _ptr(delta), rows, heads, head_dim, _stream(stream)))
 
 
-def cp_attn_bwd_step(p: cp_attn_problem, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out, stream=None):
+def cp_attn_bwd_step(p: cp_attn_problem, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out, workspace=None,
+                     stream=None):
+    """workspace: a device tensor (any dtype) whose bytes serve the dK/dV split, or None."""
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib().cp_attn_bwd_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(lse), _ptr(delta),
-                                  _ptr(dq_acc), _ptr(dk_out), _ptr(dv_out), _stream(stream)))
+                                  _ptr(dq_acc), _ptr(dk_out), _ptr(dv_out), _ptr(workspace), ws_bytes,
+                                  _stream(stream)))

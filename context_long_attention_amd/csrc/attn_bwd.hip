@@ -15,9 +15,11 @@
 //    so each lane holds one key and its P / dS registers are directly the B
 //    operands of dV^T += dO^T P and dK^T += Q^T dS; dO^T and Q^T come from the
 //    row-major LDS tiles through the transposing LDS read.  dK/dV stay in
-//    registers and are written once; when an unbalanced block's items are split
-//    over several workgroups, each adds its part once at the end (atomic adds,
-//    staged through LDS).
+//    registers and are written once.  When an unbalanced block's items are split
+//    over several workgroups, the first part writes the outputs and the others
+//    write their partial sums to a caller-supplied workspace, which a small
+//    reduction kernel adds to the outputs in part order: no atomics, so the
+//    result does not depend on timing.
 //  * bwd_dq_kernel: the forward kernel's shape (8 waves, 32 query rows of one
 //    head per wave, heads of a GQA group sharing K/V tiles, four-slot ring of
 //    K/V tiles): S^T = K Q^T and dP^T = V dO^T put one query per lane, so the
@@ -25,7 +27,7 @@
 //    transposed from the same LDS tile.  Each wave owns its dQ rows and adds
 //    its sum to the accumulator once.
 // This recomputes S and dP in both kernels (7 products instead of 5) in
-// exchange for no atomic traffic and two clean streaming loops.
+// exchange for no atomics anywhere and two clean streaming loops.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -53,6 +55,7 @@ struct BwdParams {
     float* dq;
     float* dk;
     float* dv;
+    float* ws;  // split parts 1 .. kv_split-1: [kv_split - 1][n_work_kv][2][BK][D] partial dK, dV
     const int32_t* cu;
     int32_t n_docs;
     int32_t window;  // sliding window (0: none)
@@ -75,6 +78,87 @@ constexpr int kKvThreads = 64 * kKvWaves;
 constexpr int BK = kBwdKeysPerWG;  // 128 keys per workgroup
 constexpr int BQ = kBwdQRows;      // 32 query rows per tile
 constexpr int kAuxBytes = 256 * kKvWaves;  // per slot: LSE row, delta row, two dummy areas
+constexpr int kNoEnd = 0x7fffffff;
+
+// Rows q visible from key k satisfy k <= q < qend: qend is the end of k's
+// document (DOC) and k + window (sliding window, DIAG and DOC), whichever is
+// earlier; both are non-decreasing in k.
+__device__ __forceinline__ int window_end(int win, int k) { return (win > 0 && k <= kNoEnd - win) ? k + win : kNoEnd; }
+__device__ __forceinline__ int query_end(int m, int doc_end, int w_end) {
+    return (m == CP_MASK_DOC) ? min(doc_end, w_end) : (m == CP_MASK_DIAG_CAUSAL ? w_end : kNoEnd);
+}
+
+// Key block b of a dK/dV launch (BK keys of KV head g, blocks KV-head-minor)
+// and its items: the (query head of the group, BQ-row query tile) pairs that
+// see one of its keys, n0 + (thi[1] - tlo[1]) tiles per head over the two
+// query segments, n_all in all.  The dK/dV kernel walks these items and the
+// reduction kernel recounts them.
+struct KvBlock {
+    int g, s, kt_in, key_row0, kpos0, kcount;
+    bool any_doc;
+    int kend_first, kend_last;  // document ends of the first and last key (DOC pairs)
+    int tlo[2], thi[2];
+    int n0, per_head, n_all;
+};
+
+__device__ __forceinline__ KvBlock kv_block(const BwdParams& p, int b) {
+    KvBlock k;
+    k.g = b % p.hkv;
+    const int kt = b / p.hkv;
+    k.s = (kt < p.ktiles0) ? 0 : 1;
+    k.kt_in = k.s ? kt - p.ktiles0 : kt;
+    k.key_row0 = p.ks_row0[k.s] + k.kt_in * BK;
+    k.kpos0 = p.ks_pos0[k.s] + k.kt_in * BK;
+    k.kcount = min(BK, p.ks_len[k.s] - k.kt_in * BK);
+    const int k0p = k.kpos0, k1p = k.kpos0 + k.kcount - 1;
+    k.any_doc = false;
+    for (int qs = 0; qs < p.nq_seg; ++qs) k.any_doc |= (p.mask[qs][k.s] == CP_MASK_DOC);
+    k.kend_first = k.kend_last = kNoEnd;
+    if (k.any_doc) {
+        k.kend_first = p.cu[doc_index(p.cu, p.n_docs, k0p) + 1];
+        k.kend_last = p.cu[doc_index(p.cu, p.n_docs, k1p) + 1];
+    }
+    const int wend_last = window_end(p.window, k1p);
+#pragma unroll
+    for (int qs = 0; qs < 2; ++qs) {
+        k.tlo[qs] = k.thi[qs] = 0;
+        if (qs >= p.nq_seg) continue;
+        const int m = p.mask[qs][k.s];
+        const int plen = p.qs_len[qs], ppos = p.qs_pos0[qs];
+        const int nqt = (plen + BQ - 1) / BQ;
+        if (m == CP_MASK_SKIP || plen == 0 || k.kcount <= 0) continue;
+        if (m == CP_MASK_FULL) {
+            k.thi[qs] = nqt;
+            continue;
+        }
+        if (k0p > ppos + plen - 1) continue;  // causal: rows q >= k0p
+        const int lo = (k0p <= ppos) ? 0 : (k0p - ppos) / BQ;
+        int hi = nqt;
+        const int qe = query_end(m, k.kend_last, wend_last);  // and q < qend of the last key
+        if (qe != kNoEnd) {
+            const int qmax = qe - 1;
+            hi = (qmax < ppos) ? 0 : min(nqt, (qmax - ppos) / BQ + 1);
+        }
+        if (lo < hi) {
+            k.tlo[qs] = lo;
+            k.thi[qs] = hi;
+        }
+    }
+    k.n0 = k.thi[0] - k.tlo[0];
+    k.per_head = k.n0 + (k.thi[1] - k.tlo[1]);
+    k.n_all = k.per_head * p.group;
+    return k;
+}
+
+// Items of part `part` when a block's n_all items are split over `split`
+// workgroups: consecutive runs of ceil(n_all / split) items, so the parts that
+// have items come first and number ceil(n_all / run).
+__device__ __forceinline__ int split_run(int n_all, int split) { return (n_all + split - 1) / split; }
+__device__ __forceinline__ void part_items(int n_all, int split, int part, int& it0, int& n_it) {
+    const int run = split_run(n_all, split);
+    it0 = min(n_all, part * run);
+    n_it = min(n_all, it0 + run) - it0;
+}
 
 
 template <int D>
@@ -109,13 +193,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     if (w >= p.n_work_kv * p.kv_split) return;
     const int part = w / p.n_work_kv;
     const int b = w - part * p.n_work_kv;
-    const int g = b % p.hkv;
-    const int kt = b / p.hkv;
-    const int s = (kt < p.ktiles0) ? 0 : 1;
-    const int kt_in = s ? kt - p.ktiles0 : kt;
-    const int key_row0 = p.ks_row0[s] + kt_in * BK;
-    const int kpos0 = p.ks_pos0[s] + kt_in * BK;
-    const int kcount = min(BK, p.ks_len[s] - kt_in * BK);
+    const KvBlock kb = kv_block(p, b);
+    const int g = kb.g, s = kb.s, key_row0 = kb.key_row0, kpos0 = kb.kpos0, kcount = kb.kcount;
     // query-segment parameters as opaque scalars, selected by value below (an
     // index into the parameter block would be a scalar memory load, whose wait
     // also drains the LDS counter, at every use)
@@ -123,7 +202,7 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
     const int qrow_a = sreg(p.qs_row0[0]), qrow_b = sreg(p.qs_row0[1]);
     const int qpos_a = sreg(p.qs_pos0[0]), qpos_b = sreg(p.qs_pos0[1]);
     const int mq_a = sreg(s ? p.mask[0][1] : p.mask[0][0]), mq_b = sreg(s ? p.mask[1][1] : p.mask[1][0]);
-    const int k0p = kpos0, k1p = kpos0 + kcount - 1;
+    const int k1p = kpos0 + kcount - 1;
     const int kk = 32 * wave + ql;  // this lane's key within the tile
     const bool key_valid = kk < kcount;
     const int kp = kpos0 + kk;
@@ -145,60 +224,25 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
         }
     }
 
-    // ---- query ends: (query q, key k) is visible iff k <= q < qend(k), with qend
-    // the end of k's document (DOC) and k + window (sliding window, DIAG and
-    // DOC), whichever is earlier; non-decreasing in k
-    bool any_doc = false;
-    for (int qs = 0; qs < p.nq_seg; ++qs) any_doc |= (p.mask[qs][s] == CP_MASK_DOC);
-    int kend_lane = 0x7fffffff, kend_first = 0x7fffffff, kend_last = 0x7fffffff;
-    if (any_doc) {
-        kend_first = p.cu[doc_index(p.cu, p.n_docs, k0p) + 1];
-        kend_last = p.cu[doc_index(p.cu, p.n_docs, k1p) + 1];
-        int j = doc_index(p.cu, p.n_docs, k0p);
+    // ---- this lane's query end (see query_end), and the block's first key's
+    int kend_lane = kNoEnd;
+    if (kb.any_doc) {
+        int j = doc_index(p.cu, p.n_docs, kpos0);
         if (key_valid) {
             while (j + 1 < p.n_docs && p.cu[j + 1] <= kp) ++j;
         }
         kend_lane = p.cu[j + 1];
     }
     const int win = p.window;
-    auto win_end = [&](int k) { return (win > 0 && k <= 0x7fffffff - win) ? k + win : 0x7fffffff; };
-    const int wend_lane = win_end(kp), wend_first = win_end(k0p), wend_last = win_end(k1p);
-    auto qend = [](int m, int doc_end, int w_end) {
-        return (m == CP_MASK_DOC) ? min(doc_end, w_end) : (m == CP_MASK_DIAG_CAUSAL ? w_end : 0x7fffffff);
-    };
+    const int wend_lane = window_end(win, kp), wend_first = window_end(win, kpos0);
+    const int kend_first = kb.kend_first;
+    auto qend = [](int m, int doc_end, int w_end) { return query_end(m, doc_end, w_end); };
 
-    // ---- query tiles (per query segment) that see any key of [k0p, k1p]
-    int tlo[2] = {0, 0}, thi[2] = {0, 0};
-#pragma unroll
-    for (int qs = 0; qs < 2; ++qs) {
-        if (qs >= p.nq_seg) continue;
-        const int m = p.mask[qs][s];
-        const int plen = p.qs_len[qs], ppos = p.qs_pos0[qs];
-        const int nqt = (plen + BQ - 1) / BQ;
-        if (m == CP_MASK_SKIP || plen == 0 || kcount <= 0) continue;
-        if (m == CP_MASK_FULL) {
-            thi[qs] = nqt;
-            continue;
-        }
-        if (k0p > ppos + plen - 1) continue;  // causal: rows q >= k0p
-        const int lo = (k0p <= ppos) ? 0 : (k0p - ppos) / BQ;
-        int hi = nqt;
-        const int qe = qend(m, kend_last, wend_last);  // and q < qend of the last key
-        if (qe != 0x7fffffff) {
-            const int qmax = qe - 1;
-            hi = (qmax < ppos) ? 0 : min(nqt, (qmax - ppos) / BQ + 1);
-        }
-        if (lo < hi) {
-            tlo[qs] = lo;
-            thi[qs] = hi;
-        }
-    }
-    const int n0 = thi[0] - tlo[0];
-    const int per_head = n0 + (thi[1] - tlo[1]);
-    const int n_all = per_head * p.group;
-    // this workgroup's part of the block's items: [it0, it0 + n_it)
-    const int it0 = (int)((int64_t)n_all * part / p.kv_split);
-    const int n_it = (int)((int64_t)n_all * (part + 1) / p.kv_split) - it0;
+    // ---- this workgroup's part of the block's items: [it0, it0 + n_it)
+    const int tlo[2] = {kb.tlo[0], kb.tlo[1]};
+    const int n0 = kb.n0, per_head = kb.per_head;
+    int it0, n_it;
+    part_items(kb.n_all, p.kv_split, part, it0, n_it);
     const int qrow_bytes = p.hq * D * 2;
 
     struct Item {
@@ -350,55 +394,24 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
         }
     }
 
-    // ---- write this workgroup's dK (scaled) and dV rows, or with a split add
-    // them to the cleared outputs.  The adds go through LDS so that each atomic
-    // instruction covers 64 consecutive floats of one row rather than one float
-    // of 32 rows: every wave stages its 32 rows, half of the dims in its query
-    // slot and half in its dO slot (free once the ring has drained), as rows of
-    // D/2 floats with 16-byte chunks XOR-swizzled by row.
-    // lane-derived values of the epilogue recomputed here (from the lane count, not
-    // from registers kept through the loop)
+    // ---- write this workgroup's dK (scaled) and dV rows: the outputs for part 0
+    // (zeros if it has no items), the workspace slot of (part, block) for a later
+    // part with items.  Lane-derived values of the epilogue are recomputed here
+    // (from the lane count, not from registers kept through the loop).
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int ql_e = lane_e & 31, hl_e = lane_e >> 5, kk_e = 32 * wave + ql_e;
-    if (p.kv_split > 1) {
-        constexpr int HALF = D / 2, NCH = HALF / 4, ROWB = HALF * 4;
-        static_assert(32 * ROWB <= L::BYTES, "a ring slot holds half of a wave's rows");
-        __syncthreads();  // every wave is done with the ring
-        if (n_it > 0) {
-            char* st[2] = {pick(wave == 0, qt0, pick(wave == 1, qt1, pick(wave == 2, qt2, qt3))),
-                           pick(wave == 0, ot0, pick(wave == 1, ot1, pick(wave == 2, ot2, ot3)))};
-            const int64_t row0 = (int64_t)(key_row0 + 32 * wave) * kv_stride + (int64_t)g * D;
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                const f32x16* acc = t ? dva : dka;
-                const float mul = t ? 1.f : p.scale;
-#pragma unroll
-                for (int db = 0; db < DB; ++db)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int d = 32 * db + 8 * i + 4 * hl_e;
-                        const int ch = (d % HALF) / 4;
-                        const f32x4 x = {acc[db][4 * i] * mul, acc[db][4 * i + 1] * mul, acc[db][4 * i + 2] * mul,
-                                         acc[db][4 * i + 3] * mul};
-                        *reinterpret_cast<f32x4*>(st[d / HALF] + ql_e * ROWB + ((ch ^ (ql_e % NCH)) * 16)) = x;
-                    }
-                __syncthreads();
-                float* out = t ? p.dv : p.dk;
-                constexpr int RPI = 64 / HALF;  // rows per instruction (1 at D = 128, 2 at D = 64)
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll 4
-                    for (int r0 = 0; r0 < 32; r0 += RPI) {
-                        const int r = r0 + lane_e / HALF, dl = lane_e % HALF;
-                        const float x = *reinterpret_cast<const float*>(st[h] + r * ROWB +
-                                                                        (((dl / 4) ^ (r % NCH)) * 16) + 4 * (dl % 4));
-                        if (32 * wave + r < kcount) unsafeAtomicAdd(out + row0 + (int64_t)r * kv_stride + h * HALF + dl, x);
-                    }
-                __syncthreads();
-            }
+    if (part > 0 && n_it == 0) return;
+    if (kk_e < kcount) {
+        float* dk_row;
+        float* dv_row;
+        if (part == 0) {
+            dk_row = p.dk + (int64_t)(key_row0 + kk_e) * kv_stride + (int64_t)g * D;
+            dv_row = p.dv + (int64_t)(key_row0 + kk_e) * kv_stride + (int64_t)g * D;
+        } else {
+            float* slot = p.ws + ((int64_t)(part - 1) * p.n_work_kv + b) * (2 * BK * D);
+            dk_row = slot + (int64_t)kk_e * D;
+            dv_row = slot + (int64_t)(BK + kk_e) * D;
         }
-    } else if (kk_e < kcount) {
-        const int64_t base = (int64_t)(key_row0 + kk_e) * kv_stride + (int64_t)g * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -407,9 +420,39 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
                 const f32x4 kv4 = {dka[db][4 * i] * p.scale, dka[db][4 * i + 1] * p.scale,
                                    dka[db][4 * i + 2] * p.scale, dka[db][4 * i + 3] * p.scale};
                 const f32x4 vv4 = {dva[db][4 * i], dva[db][4 * i + 1], dva[db][4 * i + 2], dva[db][4 * i + 3]};
-                *reinterpret_cast<f32x4*>(p.dk + base + d0) = kv4;
-                *reinterpret_cast<f32x4*>(p.dv + base + d0) = vv4;
+                *reinterpret_cast<f32x4*>(dk_row + d0) = kv4;
+                *reinterpret_cast<f32x4*>(dv_row + d0) = vv4;
             }
+    }
+}
+
+// Second pass of a split dK/dV step: for every key block whose items were
+// spread over more than one workgroup, add the partial sums of parts 1, 2, ...
+// (in that order) from the workspace to the outputs, which hold part 0's.
+// One workgroup per key block; rows past the block's keys are not touched.
+template <int D>
+__global__ __launch_bounds__(256) void dkdv_reduce_kernel(const BwdParams p) {
+    const int b = blockIdx.x;
+    if (b >= p.n_work_kv) return;
+    const KvBlock kb = kv_block(p, b);
+    const int run = split_run(kb.n_all, p.kv_split);
+    const int n_parts = (run > 0) ? (kb.n_all + run - 1) / run : 0;
+    if (n_parts <= 1) return;
+    const int64_t kv_stride = (int64_t)p.hkv * D;
+    constexpr int V4 = D / 4;
+    for (int i = threadIdx.x; i < BK * V4; i += blockDim.x) {
+        const int key = i / V4, d = 4 * (i % V4);
+        if (key >= kb.kcount) break;
+        const int64_t at = (int64_t)(kb.key_row0 + key) * kv_stride + (int64_t)kb.g * D + d;
+        f32x4 sk = *reinterpret_cast<const f32x4*>(p.dk + at);
+        f32x4 sv = *reinterpret_cast<const f32x4*>(p.dv + at);
+        for (int part = 1; part < n_parts; ++part) {
+            const float* slot = p.ws + ((int64_t)(part - 1) * p.n_work_kv + b) * (2 * BK * D);
+            sk += *reinterpret_cast<const f32x4*>(slot + (int64_t)key * D + d);
+            sv += *reinterpret_cast<const f32x4*>(slot + (int64_t)(BK + key) * D + d);
+        }
+        *reinterpret_cast<f32x4*>(p.dk + at) = sk;
+        *reinterpret_cast<f32x4*>(p.dv + at) = sv;
     }
 }
 
@@ -669,20 +712,6 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
     }
 }
 
-// Clear rows [r0, r0 + n0) and [r1, r1 + n1) (in units of `row` floats, a
-// multiple of 4) of a and b: the dK/dV rows that split workgroups add into.
-__global__ __launch_bounds__(256) void clear_rows_kernel(float* a, float* b, int64_t r0, int64_t n0, int64_t r1,
-                                                         int64_t n1, int64_t row) {
-    const int64_t n4 = (n0 + n1) * row / 4;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t f = 4 * i;  // float index within the two runs
-        const int64_t at = (f < n0 * row) ? r0 * row + f : r1 * row + (f - n0 * row);
-        *reinterpret_cast<f32x4*>(a + at) = z;
-        *reinterpret_cast<f32x4*>(b + at) = z;
-    }
-}
-
 // CUs of the current device (2 dK/dV workgroups run on each); 256 if unknown.
 int64_t device_cus() {
     int dev = 0, n = 0;
@@ -698,6 +727,12 @@ hipError_t launch_dkdv(const BwdParams& prm, int grid, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int D>
+hipError_t launch_reduce(const BwdParams& prm, hipStream_t stream) {
+    hipLaunchKernelGGL((dkdv_reduce_kernel<D>), dim3(prm.n_work_kv), dim3(256), 0, stream, prm);
+    return hipGetLastError();
+}
+
 template <int D, int HPW>
 hipError_t launch_dq(const BwdParams& prm, int grid, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dq_kernel<D, HPW>), dim3(grid), dim3(kQThreads), 0, stream, prm);
@@ -709,11 +744,15 @@ hipError_t launch_dq(const BwdParams& prm, int grid, hipStream_t stream) {
 
 using namespace cpattn;
 
-extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v,
-                                      const void* d_o, const float* lse, const float* delta, float* dq_acc,
-                                      float* dk_out, float* dv_out, hipStream_t stream) {
+namespace cpattn {
+
+cp_status bwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v, const void* d_o,
+                   const float* lse, const float* delta, float* dq_acc, float* dk_out, float* dv_out, void* workspace,
+                   int64_t workspace_bytes, hipStream_t stream) {
     cp_status st = validate_problem(p, true);
     if (st != CP_OK) return st;
+    if (workspace_bytes < 0 || (workspace_bytes > 0 && !workspace))
+        return fail(CP_ERR_INVALID_ARG, "workspace_bytes > 0 needs a workspace pointer (and must not be negative)");
     const TileGeom gq = fwd_geom(p->hq, p->hkv);
     BwdParams prm = {};
     prm.q = static_cast<const uint16_t*>(q);
@@ -725,6 +764,7 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     prm.dq = dq_acc;
     prm.dk = dk_out;
     prm.dv = dv_out;
+    prm.ws = static_cast<float*>(workspace);
     prm.cu = p->cu_seqlens;
     prm.n_docs = p->n_docs;
     prm.window = p->window;
@@ -774,34 +814,40 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
     if (work_kv == 0 && work_q == 0) return CP_OK;
     if (!q || !k || !v || !d_o || !lse || !delta || !dq_acc || !dk_out || !dv_out)
         return fail(CP_ERR_INVALID_ARG, "NULL tensor pointer");
-    if (!all_aligned16({q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out}))
-        return fail(CP_ERR_INVALID_ARG, "tensor pointer not 16-byte aligned");
+    if (!all_aligned16({q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out, workspace}))
+        return fail(CP_ERR_INVALID_ARG, "tensor or workspace pointer not 16-byte aligned");
     if (work_kv > (int64_t(1) << 30) || work_q > (int64_t(1) << 30))
         return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     prm.n_work_kv = int32_t(work_kv);
     prm.n_hb = p->hq / gq.hpw;
-    prm.kv_split = (p->kv_split > 0) ? p->kv_split : dkdv_split(p, nullptr, device_cus());
+    // the dK/dV split: as asked (with room for it in the workspace), or chosen
+    // here and reduced to 1 when the workspace cannot hold its parts
+    int32_t split = p->kv_split;
+    if (split > 0) {
+        if (dkdv_workspace_bytes(p, split) > workspace_bytes)
+            return fail(CP_ERR_INVALID_ARG, "kv_split " + std::to_string(split) + " needs " +
+                                                std::to_string(dkdv_workspace_bytes(p, split)) +
+                                                " workspace bytes (cp_bwd_workspace_size), got " +
+                                                std::to_string(workspace_bytes));
+    } else {
+        split = dkdv_split(p, nullptr, device_cus());
+        if (dkdv_workspace_bytes(p, split) > workspace_bytes) split = 1;
+    }
+    prm.kv_split = split;
     prm_q.n_work_kv = prm.n_work_kv;
     prm_q.n_hb = prm.n_hb;
     prm_q.kv_split = prm.kv_split;
     prm_q.n_work_q = int32_t(work_q);
     if (work_kv * prm.kv_split > (int64_t(1) << 30)) return fail(CP_ERR_UNSUPPORTED, "problem too large for one launch");
     hipError_t e = hipSuccess;
-    if (work_kv > 0 && prm.kv_split > 1) {
-        // split workgroups add into dK/dV: clear the rows of both KV segments first
-        const int64_t row = int64_t(p->hkv) * p->head_dim;
-        const int64_t n0 = prm.ks_len[0], n1 = prm.ks_len[1];
-        const int64_t n4 = (n0 + n1) * row / 4;
-        const int blocks = int(std::min<int64_t>(ceil_div(n4, 256), 4096));
-        hipLaunchKernelGGL(clear_rows_kernel, dim3(blocks), dim3(256), 0, stream, dk_out, dv_out,
-                           int64_t(prm.ks_row0[0]), n0, int64_t(prm.ks_row0[1]), n1, row);
-        e = hipGetLastError();
-        if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("dK/dV clear launch: ") + hipGetErrorString(e));
-    }
     if (work_kv > 0) {
         const int grid = int(work_kv * prm.kv_split);
         e = (p->head_dim == 128) ? launch_dkdv<128>(prm, grid, stream) : launch_dkdv<64>(prm, grid, stream);
         if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd dK/dV launch: ") + hipGetErrorString(e));
+        if (prm.kv_split > 1) {
+            e = (p->head_dim == 128) ? launch_reduce<128>(prm, stream) : launch_reduce<64>(prm, stream);
+            if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("dK/dV reduction launch: ") + hipGetErrorString(e));
+        }
     }
     if (work_q > 0) {
         const int grid = int(work_q);
@@ -814,4 +860,13 @@ extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, c
         if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("bwd dQ launch: ") + hipGetErrorString(e));
     }
     return CP_OK;
+}
+
+}  // namespace cpattn
+
+extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v,
+                                      const void* d_o, const float* lse, const float* delta, float* dq_acc,
+                                      float* dk_out, float* dv_out, void* workspace, int64_t workspace_bytes,
+                                      hipStream_t stream) {
+    return bwd_step(p, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out, workspace, workspace_bytes, stream);
 }

@@ -41,6 +41,7 @@
 #include <cstdint>
 #include <type_traits>
 
+#include "cpattn_diag.h"
 #include "internal.h"
 #include "tiles.h"
 

@@ -165,10 +165,12 @@ int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_c
     }
     // Makespan of the launch in item times when workgroup w starts on the first
     // free slot in id order (two dK/dV workgroups per CU): part w / n_blocks of
-    // block w mod n_blocks, whose key blocks run KV-head-minor.  A workgroup also
-    // costs a fixed overhead (its K/V rows, the ring's fill and drain, the output
-    // writes: about kWgOverhead items, one more with a split) and an empty one
-    // half an item.
+    // block w mod n_blocks, whose key blocks run KV-head-minor, with the items of
+    // a block in runs of ceil(items / split) per part.  A workgroup also costs a
+    // fixed overhead (its K/V rows, the ring's fill and drain, the output
+    // writes: about kWgOverhead items) and an empty one half an item.  A split
+    // adds the reduction pass, which reads every slot of a block with more than
+    // one part (and the outputs once more): kReduceSlotCost item times each.
     const int64_t slots = 2 * std::max<int64_t>(1, n_cu);
     const int64_t n_blocks = int64_t(items.size()) * p->hkv;
     if (n_blocks == 0 || n_blocks * kMaxKvSplit > (int64_t(1) << 22)) return 1;
@@ -178,8 +180,10 @@ int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_c
         for (int64_t w = 0; w < split * n_blocks; ++w) {
             const int64_t part = w / n_blocks, kt = (w % n_blocks) / p->hkv;
             const int64_t n = items[kt];
-            const int64_t mine = n * (part + 1) / split - n * part / split;
-            const double cost = mine ? double(mine) + kWgOverhead + (split > 1 ? 1.0 : 0.0) : 0.5;
+            const int64_t run = (n + split - 1) / split;
+            const int64_t it0 = std::min(n, part * run);
+            const int64_t mine = std::min(n, it0 + run) - it0;
+            const double cost = mine ? double(mine) + kWgOverhead : 0.5;
             double start = 0.0;
             if (int64_t(free_at.size()) == slots) {
                 start = free_at.top();
@@ -187,6 +191,15 @@ int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_c
             }
             free_at.push(start + cost);
             end = std::max(end, start + cost);
+        }
+        if (split > 1) {
+            double reads = 0.0;
+            for (int64_t n : items) {
+                const int64_t run = (n + split - 1) / split;
+                const int64_t parts = run ? (n + run - 1) / run : 0;
+                if (parts > 1) reads += double(parts + 1) * double(p->hkv);
+            }
+            end += kReduceSlotCost * reads;
         }
         return end;
     };
@@ -408,6 +421,16 @@ cp_status cp_bwd_kv_split(const cp_attn_problem* p, int32_t n_cu, int32_t* split
     cp_status st = validate_problem(p, false);
     if (st != CP_OK) return st;
     *split_out = dkdv_split(p, p->cu_seqlens, n_cu);
+    return CP_OK;
+}
+
+cp_status cp_bwd_workspace_size(const cp_attn_problem* p, int32_t kv_split, int64_t* bytes_out) {
+    if (!bytes_out) return fail(CP_ERR_INVALID_ARG, "bytes_out is NULL");
+    if (kv_split < 1 || kv_split > kMaxKvSplit)
+        return fail(CP_ERR_INVALID_ARG, "kv_split must be in [1, " + std::to_string(kMaxKvSplit) + "]");
+    cp_status st = validate_problem(p, true);
+    if (st != CP_OK) return st;
+    *bytes_out = dkdv_workspace_bytes(p, kv_split);
     return CP_OK;
 }
 

@@ -26,11 +26,15 @@ TileGeom fwd_geom(int hq, int hkv);
 // and walks query tiles of bmq rows.
 constexpr int kBwdKeysPerWG = 128;
 constexpr int kBwdQRows = 32;
-// A key block's query items may be spread over up to kMaxKvSplit workgroups,
-// each adding its part of dK/dV.  kWgOverhead: the fixed cost of a dK/dV
-// workgroup in item times (used to choose the split).
+// A key block's query items may be spread over up to kMaxKvSplit workgroups;
+// the first writes dK/dV, the others a workspace slot each, summed into dK/dV
+// in part order by a second pass.  kWgOverhead: the fixed cost of a dK/dV
+// workgroup in item times; kReduceSlotCost: the chip-wide cost of the second
+// pass per slot it reads (2 x 128 rows x head_dim floats), in item times (used
+// to choose the split).
 constexpr int kMaxKvSplit = 8;
 constexpr double kWgOverhead = 3.0;
+constexpr double kReduceSlotCost = 0.03;
 
 void set_error(const std::string& msg);
 cp_status fail(cp_status s, const std::string& msg);
@@ -85,6 +89,16 @@ int64_t row_lower_bound(const cp_attn_problem* p, int mask, int64_t q);
 // from the items of every block (the ranges that kernel walks) and the CU
 // count.  host_cu: host cu_seqlens for DOC masks; NULL with a DOC mask gives 1.
 int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_cu);
+
+// Workspace bytes a backward step with dK/dV split `split` needs: one slot of
+// 2 * kBwdKeysPerWG * head_dim floats (partial dK and dV) per key block of
+// every KV head, for each part after the first.  0 for split <= 1.
+inline int64_t dkdv_workspace_bytes(const cp_attn_problem* p, int32_t split) {
+    if (split <= 1) return 0;
+    int64_t blocks = 0;
+    for (int j = 0; j < p->n_kv_seg; ++j) blocks += ceil_div(p->kv_seg[j].len, kBwdKeysPerWG);
+    return int64_t(split - 1) * blocks * p->hkv * 2 * kBwdKeysPerWG * p->head_dim * int64_t(sizeof(float));
+}
 
 // The problem restricted to its query segments that pair with some KV rows
 // (a mask other than SKIP against a non-empty KV segment), in their order;

@@ -46,6 +46,7 @@ class RankRing:
         self.packed = cu_seqlens is not None
         self._live_pairs = {}
         self._kv_split = {}
+        self._ws = None
         if self.packed:
             self.cu_host = np.ascontiguousarray(cu_seqlens, dtype=np.int32)
             self.cu_dev = torch.from_numpy(self.cu_host).to(self.device)
@@ -101,16 +102,24 @@ class RankRing:
         return self._live_pairs[src] > 0
 
     def kv_split(self, src: int) -> int:
-        """dK/dV work split of the backward step on ``src``'s block.  With packed
-        documents the library cannot see the (device) document table, so the
-        split comes from the host copy; otherwise the library chooses (0)."""
-        if not self.packed:
-            return 0
+        """dK/dV work split of the backward step on ``src``'s block, chosen by the
+        library on the host (with the host copy of the documents, which the device
+        step cannot read), so that the ring can size the workspace it needs."""
         if src not in self._kv_split:
             step = (self.rank - src) % self.R
             n_cu = torch.cuda.get_device_properties(self.device).multi_processor_count
             self._kv_split[src] = cpattn.cp_bwd_kv_split(self.problem(step, src, host_docs=True), n_cu)
         return self._kv_split[src]
+
+    def workspace(self, p: cpattn.cp_attn_problem):
+        """Device workspace for the backward step p (None when its split needs
+        none); one buffer per ring, grown when a step needs more."""
+        if p.kv_split <= 1:
+            return None
+        need = cpattn.cp_bwd_workspace_size(p, p.kv_split)
+        if self._ws is None or self._ws.numel() < need:
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.device)
+        return self._ws
 
     def step_pairs(self, step: int) -> int:
         """Visible (query, key) pairs per query head at ``step`` (host count)."""
@@ -206,9 +215,10 @@ class RankRing:
                 dv = torch.empty_like(dk)
             p = self.problem(t, src)
             p.kv_split = self.kv_split(src)
+            ws = self.workspace(p)
             if timer:
                 timer(t, "bwd_begin", compute)
-            cpattn.cp_attn_bwd_step(p, q, k, v, d_o, lse, delta, dq, dk, dv, stream=compute)
+            cpattn.cp_attn_bwd_step(p, q, k, v, d_o, lse, delta, dq, dk, dv, workspace=ws, stream=compute)
             if timer:
                 timer(t, "bwd_end", compute)
             feeder.release(i, compute)

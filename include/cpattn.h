@@ -30,7 +30,11 @@
  *     launch nothing when they return an error.
  *   - Supported: D in {64, 128}; Hq % Hkv == 0; positions and rows < 2^31.
  *   - Thread-safe; no global state beyond the last-error string, which is
- *     thread-local.
+ *     thread-local.  (The diagnostics call in cpattn_diag.h is the one
+ *     exception: a process-wide recording switch, off unless set.)
+ *   - Calls marked "Helper" are not steps of the method: the pages define no
+ *     such operation; they expose the library's own tiling and work split so
+ *     that callers and tests can size buffers and check the kernels' choices.
  */
 #ifndef CPATTN_H
 #define CPATTN_H
@@ -42,7 +46,7 @@
 extern "C" {
 #endif
 
-#define CPATTN_ABI_VERSION 4
+#define CPATTN_ABI_VERSION 5
 
 typedef enum cp_status {
     CP_OK = 0,
@@ -107,9 +111,11 @@ typedef struct cp_attn_problem {
     /* Backward only: the number of workgroups (1..8) over which the dK/dV
      * kernel spreads each 128-key block's query tiles; 0 = chosen by the
      * library from the positions (1 when a mask is DOC, whose ranges need the
-     * documents on the host: see cp_bwd_kv_split).  Above 1, dK/dV are
-     * cleared and then summed in fp32 with atomic adds, so their last bits may
-     * vary between runs.  The forward calls ignore it. */
+     * documents on the host: see cp_bwd_kv_split).  Above 1, the first part
+     * of a block writes dK/dV and each later part with tiles writes its
+     * partial sums to the caller's workspace (cp_bwd_workspace_size); a second
+     * pass adds them to dK/dV in part order.  No atomics: results are the same
+     * bits on every run.  The forward calls ignore it. */
     int32_t kv_split;
 } cp_attn_problem;
 
@@ -156,13 +162,15 @@ cp_status cp_step_masks(int32_t cp_size, int32_t rank, int32_t step, int32_t pac
 cp_status cp_step_masks_window(int64_t seq_len, int32_t cp_size, int32_t rank, int32_t step, int32_t packed,
                                int64_t window, int32_t mask_out[4]);
 
-/* Tile shape of the forward kernel for this head configuration: bm query rows
- * x bn keys.  The block map and tile_map_out use this shape.  UNSUPPORTED for
- * head_dim not in {64, 128}. */
+/* Helper.  Tile shape of the forward kernel for this head configuration: bm
+ * query rows x bn keys (bm depends on the head counts, which decide how many
+ * heads of a GQA group share a workgroup).  The block map and tile_map_out use
+ * this shape.  UNSUPPORTED for head_dim not in {64, 128}. */
 cp_status cp_tile_shape(int32_t hq, int32_t hkv, int32_t head_dim, int32_t* bm_out, int32_t* bn_out);
 
-/* Size of a step's block map: query tiles (over both query segments, each
- * segment tiled from its first row, last tile possibly short) and key tiles. */
+/* Helper.  Size of a step's block map: query tiles (over both query segments,
+ * each segment tiled from its first row, last tile possibly short) and key
+ * tiles. */
 cp_status cp_block_map_size(const cp_attn_problem* p, int64_t* n_q_tiles, int64_t* n_k_tiles);
 
 /* Host computation of the block map the forward kernel follows: map_out (host,
@@ -172,8 +180,10 @@ cp_status cp_block_map_size(const cp_attn_problem* p, int64_t* n_q_tiles, int64_
  * fully masked blocks are skipped).  cu_seqlens is a host pointer here. */
 cp_status cp_block_map(const cp_attn_problem* p, uint8_t* map_out);
 
-/* Number of visible (query, key) pairs of the step, per query head (host;
- * cu_seqlens is a host pointer here). */
+/* Helper.  Number of visible (query, key) pairs of the step, per query head
+ * (host; cu_seqlens is a host pointer here): the step's causal-counted work,
+ * and zero for a block that none of the local queries can see (a ring need not
+ * receive or compute it). */
 cp_status cp_count_pairs(const cp_attn_problem* p, int64_t* pairs_out);
 
 /* -------------------------------------------------------------- device ---- */
@@ -241,22 +251,30 @@ cp_status cp_merge_partials_n(float* o_out, float* lse_out, const float* const* 
 cp_status cp_attn_fwd_step_merge(const cp_attn_problem* p, const void* q, const void* k, const void* v,
                                  float* o_acc, float* lse_acc, uint8_t* tile_map_out, hipStream_t stream);
 
-/* Diagnostics, not part of the method.  While dev_buf (device memory of
- * `capacity` uint64 values) is set, every forward step launch (cp_attn_fwd_step,
- * cp_attn_fwd_step_merge) records, for each of its first capacity / 4
- * workgroups b, four values at dev_buf[4b .. 4b+3]: the shader cycle counter and
- * the constant 100 MHz counter when the workgroup starts, then the same two when
- * it ends; the ratio of the differences gives the shader clock the work ran at.
- * Each launch overwrites the records of its workgroups.  NULL (the default)
- * turns recording off.  The setting is process-wide and read at launch time.
- * Returns CP_ERR_INVALID_ARG for a non-NULL buffer with capacity < 4. */
-cp_status cp_debug_clock_probe(uint64_t* dev_buf, int64_t capacity);
-
 /* Backward preprocessing: delta[h, i] = sum_d dO[i, h, d] * O[i, h, d] with
- * the final merged O.  d_o device bf16 [rows, heads, D]; o device fp32
- * [rows, heads, D]; delta device fp32 [heads, rows] (overwritten). */
+ * the final merged O.  The pages give no backward formulas: this is the row
+ * term of the exact softmax gradient (dS = P (dP - delta)) that the per-step
+ * backward below needs, computed once per row from the merged output.
+ * d_o device bf16 [rows, heads, D]; o device fp32 [rows, heads, D]; delta
+ * device fp32 [heads, rows] (overwritten).  INVALID_ARG on a NULL or
+ * misaligned pointer or a bad size. */
 cp_status cp_attn_bwd_prep(const void* d_o, const float* o, float* delta, int64_t rows, int32_t heads,
                            int32_t head_dim, hipStream_t stream);
+
+/* Helper.  Split of the dK/dV work that cp_attn_bwd_step would choose for
+ * kv_split = 0, computed here with HOST cu_seqlens, so DOC problems can be
+ * balanced too: a key block that many more query tiles see than an even share
+ * of the GPU's dK/dV slots (2 per CU, n_cu CUs) is spread over up to 8
+ * workgroups.  Such blocks occur where visibility is a band or a triangle
+ * (sliding windows, the edge of a document).  Writes 1..8 to split_out.
+ * INVALID_ARG on a bad problem, n_cu < 1 or a NULL split_out. */
+cp_status cp_bwd_kv_split(const cp_attn_problem* p, int32_t n_cu, int32_t* split_out);
+
+/* Helper.  Workspace bytes cp_attn_bwd_step needs for the dK/dV split kv_split
+ * (1..8) of problem p: (kv_split - 1) slots of 2 x 128 x head_dim floats per
+ * 128-key block of every KV head; 0 for kv_split = 1.  INVALID_ARG on a bad
+ * problem, a kv_split outside [1, 8] or a NULL bytes_out. */
+cp_status cp_bwd_workspace_size(const cp_attn_problem* p, int32_t kv_split, int64_t* bytes_out);
 
 /* Backward of one ring step ("Announcing Long-Context Training ...", section
  * "Built on a fast attention kernel": the ring runs the kernel per step in the
@@ -269,19 +287,20 @@ cp_status cp_attn_bwd_prep(const void* d_o, const float* o, float* delta, int64_
  *   dq_acc   device fp32 [q_rows, Hq, D]   ACCUMULATED (+=) across steps
  *   dk_out, dv_out device fp32 [kv_rows, Hkv, D]  OVERWRITTEN: this step's
  *            contribution of the local queries to the visiting block; rows
- *            outside every KV segment are not written. */
-/* Split of the dK/dV work that cp_attn_bwd_step would choose for kv_split = 0,
- * computed here with HOST cu_seqlens, so DOC problems can be balanced too: a
- * key block that many more query tiles see than an even share of the GPU's
- * dK/dV slots (2 per CU, n_cu CUs) is spread over up to 8 workgroups.  Such
- * blocks occur where visibility is a band or a triangle (sliding windows, the
- * edge of a document).  Writes 1..8 to split_out.  INVALID_ARG on a bad
- * problem, n_cu < 1 or a NULL split_out. */
-cp_status cp_bwd_kv_split(const cp_attn_problem* p, int32_t n_cu, int32_t* split_out);
-
+ *            outside every KV segment are not written.
+ *   workspace  device memory of workspace_bytes bytes (16-byte aligned; may be
+ *            NULL with 0 bytes), caller-owned, used only by the dK/dV split:
+ *            p->kv_split > 1 needs cp_bwd_workspace_size bytes (INVALID_ARG
+ *            otherwise); with p->kv_split = 0 the library's choice falls back
+ *            to 1 when the workspace is too small.  Its contents need no
+ *            initial value and are not meaningful afterwards; calls that share
+ *            one workspace must be ordered (e.g. on one stream).
+ * dQ, dK and dV are the same bits on every run: nothing is summed in an order
+ * that depends on timing. */
 cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v,
                            const void* d_o, const float* lse, const float* delta, float* dq_acc,
-                           float* dk_out, float* dv_out, hipStream_t stream);
+                           float* dk_out, float* dv_out, void* workspace, int64_t workspace_bytes,
+                           hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -129,10 +129,12 @@ SPLIT_CASES = [
 
 @pytest.mark.parametrize("name,S,R,hq,hkv,d,window,packed,rank", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
 def test_dkdv_split_matches_oracle(name, S, R, hq, hkv, d, window, packed, rank):
-    """Each key block's query tiles spread over 2, 3 or 8 workgroups that add
-    into cleared dK/dV: every step's dK/dV match the oracle (outputs pre-filled
-    with garbage, so the clear is checked too) and dQ is bit-identical to the
-    unsplit step."""
+    """Each key block's query tiles spread over 2, 3 or 8 workgroups, the later
+    parts' sums added to dK/dV from the workspace in part order: every step's
+    dK/dV match the oracle (outputs pre-filled with garbage, so every row is
+    written; the workspace pre-filled with NaN, so no slot is read that was not
+    written), the same bits come out of a second run, and dQ is bit-identical to
+    the unsplit step."""
     from context_long_attention_amd import cpattn
     cu = np.array([0, 1, 2, 130, 131, 300, 301, 520, 767, 768], dtype=np.int32) if packed else None
     w = inputs.Workload(name, S, R, hq, hkv, d, backward=True, packed=packed, window=window)
@@ -145,22 +147,31 @@ def test_dkdv_split_matches_oracle(name, S, R, hq, hkv, d, window, packed, rank)
     rows = 2 * w.chunk
     delta = torch.empty((w.hq, rows), device="cuda")
     cpattn.cp_attn_bwd_prep(inp.do, o, delta, rows, w.hq, w.dim)
+
+    def step(p, k, v, split):
+        p.kv_split = split
+        need = cpattn.cp_bwd_workspace_size(p, split)
+        ws = torch.full((max(need // 4, 1),), float("nan"), device="cuda") if need else None
+        dq = torch.zeros((rows, w.hq, w.dim), device="cuda")
+        dk = torch.full((rows, w.hkv, w.dim), 7.0, device="cuda")
+        dv = torch.full_like(dk, 7.0)
+        cpattn.cp_attn_bwd_step(p, inp.q, k, v, inp.do, lse, delta, dq, dk, dv, workspace=ws)
+        torch.cuda.synchronize()
+        return dq, dk, dv
+
     for t, src in enumerate(sched):
         k, v = inp.kv_of_source(src)
         p = ring.problem(t, src)
         outs = {}
         for split in (1, 2, 3, 8):
             note(f"split {name} step {t} kv_split={split}")
-            p.kv_split = split
-            dq = torch.zeros((rows, w.hq, w.dim), device="cuda")
-            dk = torch.full((rows, w.hkv, w.dim), 7.0, device="cuda")
-            dv = torch.full_like(dk, 7.0)
-            cpattn.cp_attn_bwd_step(p, inp.q, k, v, inp.do, lse, delta, dq, dk, dv)
-            torch.cuda.synchronize()
-            outs[split] = (dq, dk, dv)
+            outs[split] = step(p, k, v, split)
             rdk, rdv = rsteps[t]
-            assert_o_close(dk.cpu().numpy(), rdk, f"dK step {t} split {split}")
-            assert_o_close(dv.cpu().numpy(), rdv, f"dV step {t} split {split}")
+            assert_o_close(outs[split][1].cpu().numpy(), rdk, f"dK step {t} split {split}")
+            assert_o_close(outs[split][2].cpu().numpy(), rdv, f"dV step {t} split {split}")
+            again = step(p, k, v, split)
+            for a, b, what in zip(again, outs[split], ("dQ", "dK", "dV")):
+                assert torch.equal(a, b), f"{what} differs between two runs with split {split} at step {t}"
         for split in (2, 3, 8):
             assert torch.equal(outs[split][0], outs[1][0]), f"dQ changed with split {split} at step {t}"
             for a, b in zip(outs[split][1:], outs[1][1:]):
@@ -278,17 +289,28 @@ def test_dead_query_segments_left_out(masks):
     assert_o_close(dv.cpu().numpy(), rdv, "dV")
 
 
-def test_ring_is_deterministic():
-    """Two runs of the same forward and backward ring give bit-identical O, LSE,
-    dQ and per-step dK/dV (no atomics without the dK/dV split, which is forced
-    off here; with it, only the last bits of dK/dV may vary)."""
+DETERMINISM_CASES = [
+    # name, S, R, Hq, Hkv, D, window, documents, rank
+    ("dense", 2 * 4 * 96, 4, 8, 2, 128, 0, None, 1),
+    ("packed", 768, 4, 8, 2, 128, 0, [0, 1, 2, 130, 131, 300, 301, 520, 767, 768], 1),
+    ("window", 2 * 4 * 192, 4, 8, 2, 128, 64, None, 0),
+]
+
+
+@pytest.mark.parametrize("name,S,R,hq,hkv,d,window,cu,rank", DETERMINISM_CASES, ids=[c[0] for c in DETERMINISM_CASES])
+def test_ring_is_deterministic(name, S, R, hq, hkv, d, window, cu, rank):
+    """Two runs of the same forward and backward ring, with the library's default
+    dK/dV split (which splits some steps of each case), give bit-identical O, LSE,
+    dQ and per-step dK/dV."""
     from context_long_attention_amd.ring import RankRing
-    w = inputs.Workload("det", 2 * 4 * 96, 4, 8, 2, 128, backward=True)
-    inp = RankInputs(w, 1, want_do=True)
+    cu = None if cu is None else np.asarray(cu, dtype=np.int32)
+    w = inputs.Workload(name, S, R, hq, hkv, d, backward=True, packed=cu is not None, window=window)
+    note(f"determinism {name}")
+    inp = RankInputs(w, rank, want_do=True)
     runs = []
     for _ in range(2):
-        ring = RankRing(w, 1)
-        ring.kv_split = lambda src: 1
+        ring = RankRing(w, rank, cu)
+        assert max(ring.kv_split(s) for s in ring.schedule()) > 1
         o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
         dq, steps = ring.backward(inp.q, inp.do, o, lse, inp.kv_of_source)
         torch.cuda.synchronize()

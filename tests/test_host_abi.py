@@ -1,4 +1,4 @@
-"""CPU tests of libcpattn.so: it loads, exports every symbol include/cpattn.h
+"""CPU tests of libcpattn.so: it loads, exports every symbol include/*.h
 declares, its host integer logic (partition, ring order, chunk classes, block
 map, pair counts) is bit-exact against the oracle's brute force, and bad
 arguments are rejected before any launch.  No kernel runs here."""
@@ -17,6 +17,8 @@ from context_long_attention_amd import inputs
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "cpattn.h")
+HEADERS = sorted(os.path.join(ROOT, "include", f) for f in os.listdir(os.path.join(ROOT, "include"))
+                 if f.endswith(".h"))
 
 
 @pytest.fixture(scope="module")
@@ -25,14 +27,16 @@ def lib():
 
 
 def _declared():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(cp_[a-z_0-9]+)\s*\(", text)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(cp_[a-z_0-9]+)\s*\(", text))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol(lib):
     declared = _declared()
-    assert len(declared) >= 14
+    assert len(declared) >= 14 and len(HEADERS) >= 2
     assert sorted(cpattn.EXPORTS) == declared
     for name in declared:
         assert hasattr(lib, name), name
@@ -146,7 +150,7 @@ def test_validation_rejects_bad_problems(lib):
     p = cpattn.make_problem(**dict(good, head_dim=80))
     assert lib.cp_attn_fwd_step(ctypes.byref(p), None, None, None, None, None, None, None) == cpattn.CP_ERR_UNSUPPORTED
     assert lib.cp_attn_bwd_step(ctypes.byref(p), None, None, None, None, None, None, None, None, None,
-                                None) == cpattn.CP_ERR_UNSUPPORTED
+                                None, 0, None) == cpattn.CP_ERR_UNSUPPORTED
     assert lib.cp_merge_partials(None, None, None, None, -1, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
     assert lib.cp_merge_partials(None, None, None, None, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
     for n in (0, 65):
@@ -169,7 +173,19 @@ def test_validation_rejects_bad_problems(lib):
     assert b"aligned" in lib.cp_last_error()
     assert lib.cp_attn_fwd_step_merge(ctypes.byref(p), ok, ok, ok, ok, bad, None, None) == cpattn.CP_ERR_INVALID_ARG
     assert lib.cp_attn_bwd_step(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, ok, bad,
-                                None) == cpattn.CP_ERR_INVALID_ARG
+                                None, 0, None) == cpattn.CP_ERR_INVALID_ARG
+    assert lib.cp_attn_bwd_step(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, ok, ok,
+                                bad, 1 << 20, None) == cpattn.CP_ERR_INVALID_ARG  # misaligned workspace
+    assert lib.cp_attn_bwd_step(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, ok, ok,
+                                None, 64, None) == cpattn.CP_ERR_INVALID_ARG  # bytes without a workspace
+    # an explicit split needs its workspace: refused before any launch when it is short
+    p.kv_split = 2
+    need = cpattn.cp_bwd_workspace_size(p, 2)
+    assert need > 0
+    assert lib.cp_attn_bwd_step(ctypes.byref(p), ok, ok, ok, ok, ok, ok, ok, ok, ok,
+                                ok, need - 16, None) == cpattn.CP_ERR_INVALID_ARG
+    assert b"workspace" in lib.cp_last_error()
+    p.kv_split = 0
     assert lib.cp_merge_partials(ok, ok, bad, ok, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
     arr = lambda *a: (ctypes.c_void_p * len(a))(*a)
     assert lib.cp_merge_partials_n(ok, ok, arr(ok, bad), arr(ok, ok), 2, 10, 4, 128, None) == cpattn.CP_ERR_INVALID_ARG
@@ -333,17 +349,35 @@ def test_kv_split_rule():
 def test_kv_split_simulated_launch():
     """One 128-key block of one KV head seen by 128 query tiles (FULL): alone it
     takes 128 items plus a fixed cost of 3; split s ways each part takes
-    128/s + 4.  With 512 slots all parts run at once (8 parts: 20 against 131);
-    with 2 slots (one CU) 2 parts take 68, 4 parts 2 x 36 and 8 parts 4 x 20."""
+    128/s + 3, and the reduction pass reads s + 1 slots at 0.03 each.  With 512
+    slots all parts run at once (8 parts: 19.3 against 131); with 2 slots (one
+    CU) 2 parts take 67.1, 4 parts 2 x 35 + 0.15 and 8 parts 4 x 19 + 0.27."""
     F, S_ = cpattn.CP_MASK_FULL, cpattn.CP_MASK_SKIP
     p = cpattn.make_problem(1, 1, 128, 0.1, 4096, 128, [(0, 0, 4096)], [(0, 5000, 128)], [[F, S_], [S_, S_]])
     assert cpattn.cp_bwd_kv_split(p, 256) == 8
     assert cpattn.cp_bwd_kv_split(p, 1) == 2
     # 256 equal workgroups (32 blocks x 8 KV heads): two full rounds on 64 CUs are
     # not split; on 256 CUs they fill half of the slots, and halves fill them all
+    # (67 per part, plus 0.03 x 3 x 256 for the reduction, against 131)
     p = cpattn.make_problem(8, 8, 128, 0.1, 4096, 4096, [(0, 0, 4096)], [(0, 5000, 4096)], [[F, S_], [S_, S_]])
     assert cpattn.cp_bwd_kv_split(p, 64) == 1
     assert cpattn.cp_bwd_kv_split(p, 256) == 2
+
+
+def test_bwd_workspace_size():
+    """(split - 1) slots of 2 x 128 x D floats per 128-key block of every KV head."""
+    F, S_ = cpattn.CP_MASK_FULL, cpattn.CP_MASK_SKIP
+    for d in (64, 128):
+        p = cpattn.make_problem(8, 2, d, 0.1, 300, 700, [(0, 0, 300)], [(0, 400, 200), (200, 900, 500)],
+                                [[F, S_], [S_, S_]])
+        blocks = (2 + 4) * 2  # ceil(200/128) + ceil(500/128) key blocks, 2 KV heads
+        assert cpattn.cp_bwd_workspace_size(p, 1) == 0
+        for split in (2, 3, 8):
+            assert cpattn.cp_bwd_workspace_size(p, split) == (split - 1) * blocks * 2 * 128 * d * 4
+        for bad in (0, 9, -1):
+            with pytest.raises(cpattn.CpError) as e:
+                cpattn.cp_bwd_workspace_size(p, bad)
+            assert e.value.status == cpattn.CP_ERR_INVALID_ARG
 
 
 def test_kv_split_validation():
