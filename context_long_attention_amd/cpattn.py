@@ -26,7 +26,7 @@ EXPORTS = (
     "cp_step_masks", "cp_step_masks_window", "cp_tile_shape", "cp_block_map_size", "cp_block_map",
     "cp_count_pairs", "cp_bwd_kv_split", "cp_bwd_workspace_size", "cp_merge_partials_n", "cp_attn_fwd_step",
     "cp_merge_partials", "cp_attn_fwd_step_merge", "cp_attn_bwd_prep", "cp_attn_bwd_step",
-    "cp_debug_clock_probe",
+    "cp_attn_bwd_step_noalloc", "cp_debug_clock_probe",
 )
 
 
@@ -88,6 +88,7 @@ def lib():
             "cp_debug_clock_probe": ([vp, i64], i32),
             "cp_attn_bwd_prep": ([vp, f32p, f32p, i64, i32, i32, vp], i32),
             "cp_attn_bwd_step": ([P, vp, vp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp, i64, vp], i32),
+            "cp_attn_bwd_step_noalloc": ([P, vp, vp, vp, vp, f32p, f32p, f32p, f32p, f32p, vp], i32),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -256,3 +257,9 @@ def cp_attn_bwd_step(p: cp_attn_problem, q, k, v, d_o, lse, delta, dq_acc, dk_ou
     _check(lib().cp_attn_bwd_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(lse), _ptr(delta),
                                   _ptr(dq_acc), _ptr(dk_out), _ptr(dv_out), _ptr(workspace), ws_bytes,
                                   _stream(stream)))
+
+
+def cp_attn_bwd_step_noalloc(p: cp_attn_problem, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out, stream=None):
+    """cp_attn_bwd_step with the library's fixed per-device scratch as the workspace."""
+    _check(lib().cp_attn_bwd_step_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(lse),
+                                          _ptr(delta), _ptr(dq_acc), _ptr(dk_out), _ptr(dv_out), _stream(stream)))

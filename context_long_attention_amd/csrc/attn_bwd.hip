@@ -31,8 +31,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <mutex>
 #include <type_traits>
 
 #include "internal.h"
@@ -862,7 +864,56 @@ cp_status bwd_step(const cp_attn_problem* p, const void* q, const void* k, const
     return CP_OK;
 }
 
+// ---------------------------------------------------------------- no-alloc variant
+// The dK/dV split's workspace for callers that cannot allocate: a fixed array in
+// the code object, one per device the library runs on, held until the process
+// ends.  Host code never names it after set-up: its address on each device comes
+// from hipGetSymbolAddress (the name itself is only a host-side stand-in).
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Address of the current device's scratch array, looked up on its first use.
+cp_status scratch_of_current_device(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(CP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(CP_ERR_UNSUPPORTED, "device index beyond 63");
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (!ptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mu);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (!ptr) {
+            e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+            if (e != hipSuccess || !ptr)
+                return fail(CP_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return CP_OK;
+}
+
 }  // namespace cpattn
+
+extern "C" cp_status cp_attn_bwd_step_noalloc(const cp_attn_problem* p, const void* q, const void* k, const void* v,
+                                              const void* d_o, const float* lse, const float* delta, float* dq_acc,
+                                              float* dk_out, float* dv_out, hipStream_t stream) {
+    cp_status st = validate_problem(p, true);
+    if (st != CP_OK) return st;
+    if (p->kv_split > 1 && dkdv_workspace_bytes(p, p->kv_split) > kScratchBytes)
+        return fail(CP_ERR_INVALID_ARG, "kv_split " + std::to_string(p->kv_split) + " needs " +
+                                            std::to_string(dkdv_workspace_bytes(p, p->kv_split)) +
+                                            " workspace bytes; the no-alloc entry point has " +
+                                            std::to_string(kScratchBytes));
+    void* ws = nullptr;
+    st = scratch_of_current_device(&ws);
+    if (st != CP_OK) return st;
+    return bwd_step(p, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out, ws, kScratchBytes, stream);
+}
 
 extern "C" cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, const void* k, const void* v,
                                       const void* d_o, const float* lse, const float* delta, float* dq_acc,

@@ -302,6 +302,22 @@ cp_status cp_attn_bwd_step(const cp_attn_problem* p, const void* q, const void* 
                            float* dk_out, float* dv_out, void* workspace, int64_t workspace_bytes,
                            hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same
+ * backward step as cp_attn_bwd_step, with the dK/dV split's workspace taken
+ * from a fixed 64 MiB array that the library holds on each device it runs on
+ * (for the life of the process) instead of from the caller.  It calls no
+ * allocator.  A p->kv_split > 1 whose workspace (cp_bwd_workspace_size)
+ * exceeds 64 MiB gives INVALID_ARG; with p->kv_split = 0 the library's choice
+ * falls back to 1 when its workspace would not fit.  The array needs no
+ * initial value and keeps whatever the last call left; calls that overlap on
+ * one GPU (other streams, other threads) share it and race, so order them.
+ * Same arguments, layouts, results and errors as cp_attn_bwd_step otherwise
+ * (CP_ERR_HIP if the array's device address cannot be looked up). */
+cp_status cp_attn_bwd_step_noalloc(const cp_attn_problem* p, const void* q, const void* k, const void* v,
+                                   const void* d_o, const float* lse, const float* delta, float* dq_acc,
+                                   float* dk_out, float* dv_out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif
