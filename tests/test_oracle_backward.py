@@ -125,3 +125,41 @@ def test_delta_is_row_dot_product():
     for h in range(3):
         for i in range(5):
             assert abs(d[h, i] - float(np.dot(do[i, h], o[i, h]))) < 1e-14
+
+
+def test_delta_equals_probability_weighted_scores():
+    """Delta_i = sum_d dO_i,d O_i,d must equal sum_j P_ij (dO_i . v_j), with P taken
+    from a library softmax of the scores (scipy), not from the oracle's forward:
+    a different route to the same row term, which a wrong index, operand or
+    reduction axis in delta_rows would break."""
+    from scipy.special import softmax
+    n, hq, hkv, d = 9, 4, 2, 6
+    q, k, v, do = _rand((n, hq, d), 20), _rand((n, hkv, d), 21), _rand((n, hkv, d), 22), _rand((n, hq, d), 23)
+    pos = np.arange(n)
+    vis = oracle.visibility(pos, pos)
+    o, _ = oracle.attention_partial(q, k, v, vis, 0.4)
+    delta = oracle.delta_rows(do, o)
+    g = hq // hkv
+    for h in range(hq):
+        s = np.where(vis, 0.4 * q[:, h] @ k[:, h // g].T, -np.inf)
+        p = softmax(s, axis=1)
+        want = (p * (do[:, h] @ v[:, h // g].T)).sum(axis=1)
+        np.testing.assert_allclose(delta[h], want, rtol=0, atol=1e-12)
+
+
+def test_delta_makes_dq_vanish_for_identical_keys():
+    """With every key identical, the scores of a row do not depend on which key
+    they belong to, so dQ = scale * sum_j dS_ij k = 0 exactly when Delta is the
+    row sum of P (dO . v): Delta from delta_rows of the oracle's own output gives
+    dQ = 0, and a perturbed Delta does not."""
+    n, hq, hkv, d = 12, 2, 1, 5
+    q, v, do = _rand((n, hq, d), 30), _rand((n, hkv, d), 31), _rand((n, hq, d), 32)
+    k = np.broadcast_to(_rand((1, hkv, d), 33), (n, hkv, d)).copy()
+    pos = np.arange(n)
+    vis = oracle.visibility(pos, pos)
+    o, lse = oracle.attention_partial(q, k, v, vis, 0.7)
+    delta = oracle.delta_rows(do, o)
+    dq, _, _ = oracle.attention_backward_partial(q, k, v, do, lse, delta, vis, 0.7)
+    np.testing.assert_allclose(dq, 0, atol=1e-12)
+    dq_bad, _, _ = oracle.attention_backward_partial(q, k, v, do, lse, delta + 0.1, vis, 0.7)
+    assert np.abs(dq_bad).max() > 1e-3
