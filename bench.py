@@ -16,6 +16,15 @@ traffic per launch from the committed FETCH_SIZE / WRITE_SIZE summary under
 profiles/, when that summary was taken on the current kernel sources (else
 null); ``--calibrate-copy-mib`` makes the known-size copies that summary is
 scaled by.
+
+Timing protocol: every timed pass of a leg is bracketed by its own pair of HIP
+events, so each leg reports the median (and min / max) over its repetitions --
+the K headline steps, 10 passes of the Llama-3-8B training and packed-document
+legs, 3 of the Llama-3-405B leg -- and the headline and training legs also give
+the median launch time of every ring step.  ``value`` itself is the whole-job
+rate over the K bracketed headline steps.  The float64 oracle is timed on the
+host on a bounded sample of the headline workload (``cpu_baseline``) and, with
+its rate extrapolated to the whole share, of the Llama-3-405B one.
 """
 from __future__ import annotations
 
@@ -139,17 +148,21 @@ def gemm_reference(torch, n=16384, reps=10):
             "pct_bf16_peak": round(100 * t / BF16_PEAK_TFLOPS, 2), "ms": round(ms, 3)}
 
 
+def blas_threads():
+    """Threads the oracle's BLAS calls use on this host."""
+    try:
+        from threadpoolctl import threadpool_info
+        return max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        return len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, rank, heads):
     """The float64 oracle on a bounded sample: ``heads`` query heads of the GQA group
     of KV head 0, every ring step of the rank, every local row."""
     import oracle
     from context_long_attention_amd import inputs
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info() if i.get("user_api") == "blas"]
-                      or [1])
-    except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
+    threads = blas_threads()
     c, R = w.chunk, w.cp
     qa, qb = oracle.zigzag_chunks(R, rank)
     qpos = oracle.zigzag_positions(w.seq_len, R, rank)
@@ -170,6 +183,41 @@ def cpu_baseline(w, rank, heads):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{w.name} rank {rank}: forward of {heads} of {w.hq} query heads (KV head 0), "
                       f"all {R} ring steps, all {2 * c} local rows, float64 NumPy; {dt:.1f} s",
+            "seconds": dt, "flops": flops}
+
+
+def cpu_baseline_extrapolated(w, rank, row_stride=4, steps=(0, 1)):
+    """The float64 oracle on a bounded sample of a share too large to run whole:
+    query head 0, every ``row_stride``-th local row, ring steps ``steps``; its rate
+    (causal-counted FLOP of the sample over the sample's time) is the baseline,
+    and the whole share's time is extrapolated from it.  K and V follow the input
+    recipe; the sampled query rows are N(0,1) draws of their own (the recipe draws
+    every head of a chunk at once, 4 GiB for a Llama-3-405B query chunk), rounded
+    to bf16 -- the oracle's work does not depend on the values."""
+    import oracle
+    from context_long_attention_amd import inputs
+    c, R = w.chunk, w.cp
+    rows = np.arange(0, 2 * c, row_stride)
+    qpos = oracle.zigzag_positions(w.seq_len, R, rank)[rows]
+    q = inputs.round_bf16(np.random.default_rng([inputs.SEED_Q, 1 << 20, rank]).standard_normal(
+        (len(rows), 1, w.dim), dtype=np.float32))
+    blocks, flops = [], 0
+    for t in steps:
+        s_ = oracle.ring_source(rank, t, R)
+        ka, kb = oracle.zigzag_chunks(R, s_)
+        kv = [np.concatenate([inputs.round_bf16(inputs.chunk_normal(seed, ch, c, w.hkv, w.dim)[:, :1])
+                              for ch in (ka, kb)]) for seed in (inputs.SEED_K, inputs.SEED_V)]
+        kpos = oracle.zigzag_positions(w.seq_len, R, s_)
+        blocks.append((kv[0], kv[1], kpos))
+        flops += oracle.causal_flops(qpos, kpos, 1, w.dim)
+    t0 = time.perf_counter()
+    oracle.rank_forward(q, qpos, blocks, None, w.scale)
+    dt = time.perf_counter() - t0
+    rate = flops / dt
+    return {"value": rate / 1e12, "unit": "TFLOP/s", "cores": blas_threads(), "kind": "oracle", "extrapolated": True,
+            "sample": f"{w.name} rank {rank}: forward of query head 0 of {w.hq}, every {row_stride}th of the "
+                      f"{2 * c} local rows, ring steps {list(steps)} of {R}, float64 NumPy; {dt:.1f} s; "
+                      f"rate extrapolated to the whole share",
             "seconds": dt, "flops": flops}
 
 
@@ -246,19 +294,27 @@ def measure(torch, w, rank, steps, warmup, backward):
     fwd_timer.enabled = bwd_timer.enabled = True
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     start.record()
-    for _ in range(steps):
+    marks[0].record()
+    for i in range(steps):
         one_step()
+        marks[i + 1].record()
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
+    rep_ms = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
     fwd_timer.enabled = bwd_timer.enabled = False
     clocks = probe_clock(torch, one_step)
     per_step = [ring.step_pairs(t) * w.hq * w.dim * 4 for t in range(w.cp)]
     launch = fwd_timer.launch_ms()
     merge_ms = [x for i, x in enumerate(launch) if i % w.cp > 0]
-    out = {"ms": ms, "fwd_kernel_ms": fwd_timer.total_ms() / steps, "flops_fwd": flops_fwd,
+    # median launch time of each ring step over the timed passes (every step of
+    # these causal rings is live, so each pass launches R forward kernels)
+    fwd_steps = np.asarray(launch).reshape(steps, w.cp)
+    out = {"ms": ms, "rep_ms": rep_ms, "fwd_step_ms": np.median(fwd_steps, axis=0).tolist(),
+           "fwd_kernel_ms": fwd_timer.total_ms() / steps, "flops_fwd": flops_fwd,
            "flops_bwd": flops_bwd if backward else 0, "launches": w.cp, "clocks": clocks,
            # the launches that merge into the accumulator (ring steps 1..R-1)
            "merge_flops_per_launch": sum(per_step[1:]) / max(1, w.cp - 1),
@@ -267,6 +323,7 @@ def measure(torch, w, rank, steps, warmup, backward):
                                          for t in range(1, w.cp)) / max(1, w.cp - 1)}
     if backward:
         out["bwd_kernel_ms"] = bwd_timer.total_ms() / steps
+        out["bwd_step_ms"] = np.median(np.asarray(bwd_timer.launch_ms()).reshape(steps, w.cp), axis=0).tolist()
     log(f"{w.name}: {steps} steps, {ms:.3f} ms/step, fwd kernels {out['fwd_kernel_ms']:.3f} ms"
         + (f", bwd kernels {out['bwd_kernel_ms']:.3f} ms" if backward else ""))
     return out
@@ -288,20 +345,28 @@ def _dev_normal(torch, shape, seed):
 
 
 def _time_leg(torch, fn, steps, warmup, timer=None):
-    """(ms per call of fn over `steps` timed calls, kernel ms per call or None)."""
+    """(ms per call of fn over `steps` timed calls, kernel ms per call or None,
+    the ms of each timed call)."""
     for _ in range(warmup):
         fn(None)
     torch.cuda.synchronize()
     if timer is not None:
         timer.enabled = True
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for i in range(steps):
         fn(timer)
-    b.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
     kern = timer.total_ms() / steps if timer is not None else None
-    return a.elapsed_time(b) / steps, kern
+    reps = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
+    return marks[0].elapsed_time(marks[-1]) / steps, kern, reps
+
+
+def rep_stats(rep_ms):
+    """Median, min and max over the timed repetitions of a leg."""
+    return {"reps": len(rep_ms), "ms_median": round(float(np.median(rep_ms)), 4),
+            "ms_min": round(float(np.min(rep_ms)), 4), "ms_max": round(float(np.max(rep_ms)), 4)}
 
 
 def measure_variants(torch, w, rank, steps, warmup):
@@ -325,7 +390,7 @@ def measure_variants(torch, w, rank, steps, warmup):
         parts = pq.forward(k, v, qs.__getitem__, stage=True, timer=timer)
         pq.restore([(o, l) for _, o, l in parts])
 
-    ms, kern = _time_leg(torch, pass_q, steps, warmup, KernelTimer(torch, "fwd"))
+    ms, kern, _ = _time_leg(torch, pass_q, steps, warmup, KernelTimer(torch, "fwd"))
     out["pass_q"] = {"workload": f"{w.name} Pass Q rank {rank}", "tflops": round(tflops(pairs * fpp, ms), 2),
                      "kernel_tflops": round(tflops(pairs * fpp, kern), 2), "ms_per_step": round(ms, 4)}
     del qs
@@ -339,7 +404,7 @@ def measure_variants(torch, w, rank, steps, warmup):
                _dev_normal(torch, (2 * pp.cn, w.hkv, w.dim), 600 + s), _dev_normal(torch, (2 * pp.cn, w.hkv, w.dim), 700 + s))
            for s in range(R)}
     pairs = sum(cpattn.cp_count_pairs(p) for t in range(R) for p in pp.problems(t))
-    ms, kern = _time_leg(torch, lambda timer: pp.forward(q_new, kvs.__getitem__, stage=True, timer=timer), steps,
+    ms, kern, _ = _time_leg(torch, lambda timer: pp.forward(q_new, kvs.__getitem__, stage=True, timer=timer), steps,
                          warmup, KernelTimer(torch, "fwd"))
     out["partial_prefill"] = {"workload": f"Llama-3-8B partial prefill, {P} cached + {N} new tokens, CP={R}, rank {rank}",
                               "tflops": round(tflops(pairs * fpp, ms), 2),
@@ -353,7 +418,7 @@ def measure_variants(torch, w, rank, steps, warmup):
     wu = usp_share(w, 2)
     uq, ukv = make_rank_inputs(torch, wu, rank)
     pairs = sum(RankRing(wu, rank).step_pairs(t) for t in range(wu.cp))
-    ms, kern = _time_leg(torch, lambda timer: RankRing(wu, rank).forward(uq, ukv.__getitem__, stage=True, timer=timer),
+    ms, kern, _ = _time_leg(torch, lambda timer: RankRing(wu, rank).forward(uq, ukv.__getitem__, stage=True, timer=timer),
                          steps, warmup, KernelTimer(torch, "fwd"))
     fpu = wu.hq * wu.dim * 4
     out["usp"] = {"workload": f"{w.name} USP share, all-to-all groups of 2: ring of {wu.cp} ranks, Hq={wu.hq}, "
@@ -368,7 +433,7 @@ def measure_variants(torch, w, rank, steps, warmup):
     k_all = _dev_normal(torch, (w.seq_len, w.hkv, w.dim), 802)
     v_all = _dev_normal(torch, (w.seq_len, w.hkv, w.dim), 803)
     ring_pairs = 2 * R * c * c + c
-    ms, _ = _time_leg(torch, lambda timer: gathered_forward(w, rank, q_loc, k_all, v_all), steps, warmup)
+    ms, _, _ = _time_leg(torch, lambda timer: gathered_forward(w, rank, q_loc, k_all, v_all), steps, warmup)
     out["all_gather"] = {"workload": f"{w.name} gathered KV, rank {rank}", "tflops": round(tflops(ring_pairs * fpp, ms), 2),
                          "ms_per_step": round(ms, 4)}
     log(f"all_gather: {ms:.3f} ms/step")
@@ -379,7 +444,7 @@ def measure_variants(torch, w, rank, steps, warmup):
     k_h = _dev_normal(torch, (w.seq_len, hkv_d, w.dim), 902)
     v_h = _dev_normal(torch, (w.seq_len, hkv_d, w.dim), 903)
     pairs = w.seq_len * (w.seq_len + 1) // 2
-    ms, _ = _time_leg(torch, lambda timer: head_sharded_forward(q_h, k_h, v_h, w.scale), steps, warmup)
+    ms, _, _ = _time_leg(torch, lambda timer: head_sharded_forward(q_h, k_h, v_h, w.scale), steps, warmup)
     out["ulysses"] = {"workload": f"{w.name} head-sharded, {hq_d} query heads / {hkv_d} KV head over {w.seq_len} tokens",
                       "tflops": round(tflops(pairs * hq_d * w.dim * 4, ms), 2), "ms_per_step": round(ms, 4)}
     log(f"ulysses: {ms:.3f} ms/step")
@@ -415,18 +480,19 @@ def measure_window(torch, w, rank, steps, warmup):
         one_step(None)
     torch.cuda.synchronize()
     fwd_timer.enabled = bwd_timer.enabled = True
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(steps):
+    marks = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    marks[0].record()
+    for i in range(steps):
         one_step(timer)
-    b.record()
+        marks[i + 1].record()
     torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / steps
+    reps = [marks[i].elapsed_time(marks[i + 1]) for i in range(steps)]
+    ms = float(np.median(reps))
     f_fwd, f_bwd = pairs * w.hq * w.dim * 4, pairs * w.hq * w.dim * 10
-    log(f"{w.name}: {ms:.3f} ms/step, live steps {live}")
+    log(f"{w.name}: {ms:.3f} ms/step (median of {steps}), live steps {live}")
     return {"workload": f"{w.name}: window {w.window} over S={w.seq_len} at CP={w.cp}, rank {rank}, fwd+bwd",
             "window": w.window, "live_steps": live, "pairs_per_head": pairs,
-            "tflops": round(tflops(f_fwd + f_bwd, ms), 2), "ms_per_step": round(ms, 4),
+            "tflops": round(tflops(f_fwd + f_bwd, ms), 2), "ms_per_step": round(ms, 4), "timing": rep_stats(reps),
             "fwd_kernel_tflops": round(tflops(f_fwd, fwd_timer.total_ms() / steps), 2),
             "bwd_kernel_tflops": round(tflops(f_bwd, bwd_timer.total_ms() / steps), 2)}
 
@@ -446,12 +512,14 @@ def measure_large(torch, w, rank, steps, warmup):
     def one(tm):
         RankRing(w, rank).forward(q, kv.__getitem__, stage=True, timer=tm)
 
-    ms, kern = _time_leg(torch, one, steps, warmup, timer)
-    log(f"{w.name}: {ms:.1f} ms per ring")
+    ms, kern, reps = _time_leg(torch, one, steps, warmup, timer)
+    med = float(np.median(reps))
+    log(f"{w.name}: {med:.1f} ms per ring (median of {steps})")
     return {"workload": f"{w.name}: Hq={w.hq} Hkv={w.hkv} D={w.dim}, rank {rank} of S={w.seq_len} at CP={w.cp}, "
                         f"{w.cp} ring steps of {w.local}-token KV blocks, fwd",
-            "tflops": round(tflops(flops, ms), 2), "pct_bf16_peak": round(100 * tflops(flops, ms) / BF16_PEAK_TFLOPS, 2),
-            "kernel_tflops": round(tflops(flops, kern), 2), "ms_per_ring": round(ms, 2)}
+            "tflops": round(tflops(flops, med), 2), "pct_bf16_peak": round(100 * tflops(flops, med) / BF16_PEAK_TFLOPS, 2),
+            "kernel_tflops": round(tflops(flops, kern), 2), "ms_per_ring": round(med, 2), "flops": flops,
+            "timing": rep_stats(reps)}
 
 
 def measure_packed(torch, w, steps, warmup):
@@ -479,15 +547,16 @@ def measure_packed(torch, w, steps, warmup):
             o, lse, _ = ring.forward(q, kv.__getitem__, stage=True, timer=tm)
             ring.backward(q, d_o, o, lse, kv.__getitem__, stage=True, keep_steps=False, timer=tm)
 
-    ms, _ = _time_leg(torch, one, steps, warmup, None)
+    ms, _, reps = _time_leg(torch, one, steps, warmup, None)
+    med = float(np.median(reps))
     fwd_t.enabled = bwd_t.enabled = True
     one(timer)
     torch.cuda.synchronize()
     f_fwd, f_bwd = pairs * w.hq * w.dim * 4, pairs * w.hq * w.dim * 10
-    log(f"{w.name}: {ms:.1f} ms for all {w.cp} ranks")
+    log(f"{w.name}: {med:.1f} ms for all {w.cp} ranks (median of {steps})")
     return {"workload": f"{w.name}: S={w.seq_len} at CP={w.cp}, {len(cu) - 1} documents, every rank's fwd+bwd ring",
             "pairs_per_head": pairs, "visible_fraction_of_causal": round(pairs / (w.seq_len * (w.seq_len + 1) / 2), 4),
-            "tflops": round(tflops(f_fwd + f_bwd, ms), 2), "ms_all_ranks": round(ms, 2),
+            "tflops": round(tflops(f_fwd + f_bwd, med), 2), "ms_all_ranks": round(med, 2), "timing": rep_stats(reps),
             "fwd_kernel_tflops": round(tflops(f_fwd, fwd_t.total_ms()), 2),
             "bwd_kernel_tflops": round(tflops(f_bwd, bwd_t.total_ms()), 2)}
 
@@ -499,7 +568,7 @@ def tflops(flops, ms):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="llama3_8b_fwd")
     ap.add_argument("--bwd-workload", default="llama3_8b_fwdbwd")
@@ -557,6 +626,9 @@ def main():
                    "local_tokens": w.local, "hq": w.hq, "hkv": w.hkv, "head_dim": w.dim,
                    "ring_steps": w.cp, "pass": "fwd"},
         "pct_bf16_peak": round(100 * value / BF16_PEAK_TFLOPS, 2),
+        "timing": dict(rep_stats(fwd["rep_ms"]),
+                       tflops_median=round(tflops(fwd["flops_fwd"], float(np.median(fwd["rep_ms"]))), 2),
+                       ring_step_ms=[round(x, 4) for x in fwd["fwd_step_ms"]]),
         "clocks": fwd["clocks"],
         "kernel_only": {"tflops": round(kernel_tflops, 2),
                         "pct_bf16_peak": round(100 * kernel_tflops / BF16_PEAK_TFLOPS, 2),
@@ -572,13 +644,16 @@ def main():
     }
     if not args.no_bwd:
         wb = inputs.WORKLOADS[args.bwd_workload]
-        fb = measure(torch, wb, args.rank, max(1, args.steps // 2), 1, backward=True)
+        fb = measure(torch, wb, args.rank, 10, 1, backward=True)
         total = fb["flops_fwd"] + fb["flops_bwd"]
+        med = float(np.median(fb["rep_ms"]))
         record["fwd_bwd"] = {
             "workload": wb.name, "seq_len": wb.seq_len, "cp": wb.cp, "ring_steps": wb.cp,
-            "tflops": round(tflops(total, fb["ms"]), 2),
-            "pct_bf16_peak": round(100 * tflops(total, fb["ms"]) / BF16_PEAK_TFLOPS, 2),
-            "ms_per_step": round(fb["ms"], 4),
+            "tflops": round(tflops(total, med), 2),
+            "pct_bf16_peak": round(100 * tflops(total, med) / BF16_PEAK_TFLOPS, 2),
+            "ms_per_step": round(med, 4),
+            "timing": dict(rep_stats(fb["rep_ms"]), fwd_ring_step_ms=[round(x, 4) for x in fb["fwd_step_ms"]],
+                           bwd_ring_step_ms=[round(x, 4) for x in fb["bwd_step_ms"]]),
             "fwd_kernel_tflops": round(tflops(fb["flops_fwd"], fb["fwd_kernel_ms"]), 2),
             "bwd_kernel_tflops": round(tflops(fb["flops_bwd"], fb["bwd_kernel_ms"]), 2),
             "bwd_kernel_ms_per_step": round(fb["bwd_kernel_ms"], 4),
@@ -587,12 +662,17 @@ def main():
     if not args.no_variants:
         record["variants"] = measure_variants(torch, w, args.rank, max(1, args.steps // 2), 1)
     if not args.no_large:
-        record["llama3_405b_fwd"] = measure_large(torch, inputs.WORKLOADS["llama3_405b_fwd"], args.rank, 1, 1)
+        wl = inputs.WORKLOADS["llama3_405b_fwd"]
+        record["llama3_405b_fwd"] = measure_large(torch, wl, args.rank, 3, 1)
+        if not args.no_cpu_baseline:
+            log("timing the float64 oracle on a sample of the Llama-3-405B share (extrapolated baseline)")
+            cb = cpu_baseline_extrapolated(wl, args.rank)
+            cb["seconds_for_share"] = round(record["llama3_405b_fwd"]["flops"] / (cb["value"] * 1e12), 1)
+            record["llama3_405b_fwd"]["cpu_baseline"] = cb
     if not args.no_packed:
-        record["llama3_8b_packed"] = measure_packed(torch, inputs.WORKLOADS["llama3_8b_packed"], 1, 1)
+        record["llama3_8b_packed"] = measure_packed(torch, inputs.WORKLOADS["llama3_8b_packed"], 10, 1)
     if not args.no_window:
-        record["sliding_window"] = measure_window(torch, inputs.WORKLOADS[args.window_workload], args.rank,
-                                                  max(1, args.steps // 2), 1)
+        record["sliding_window"] = measure_window(torch, inputs.WORKLOADS[args.window_workload], args.rank, 10, 1)
     if not args.no_gemm_reference:
         record["gemm_reference"] = gemm_reference(torch)
         record["gemm_reference"]["attention_over_gemm"] = round(value / record["gemm_reference"]["tflops"], 3)
