@@ -108,6 +108,7 @@ class Shared:
         for s, (kb, vb) in kv_bits.items():
             np.save(self._path(f"k{int(s)}"), np.ascontiguousarray(kb, dtype=np.uint16))
             np.save(self._path(f"v{int(s)}"), np.ascontiguousarray(vb, dtype=np.uint16))
+            np.save(self._path(f"p{int(s)}"), self.kpos[int(s)])
 
     def _path(self, name):
         return os.path.join(self.dir, name + ".npy")
@@ -145,9 +146,10 @@ def _f64(bits) -> np.ndarray:
     return inputs.bf16_to_f32(np.asarray(bits)).astype(np.float64)
 
 
-def _key_blocks(spec, h, src, r0, r1, kpos):
+def _key_blocks(spec, h, src, r0, r1):
     """(q, visibility, key block [c0, c1)) of a task, for every key block that one
     of its rows can see; q is float64 [r1 - r0, 1, D]."""
+    kpos = np.asarray(_bits(spec, f"p{src}"))
     q = _f64(_bits(spec, "q")[r0:r1, h:h + 1, :])
     vis = oracle.visibility(spec["qpos"][r0:r1], kpos, spec["cu"], spec["window"] or None)
     out = []
@@ -163,9 +165,9 @@ def _kv(spec, name, g, c0, c1):
     return _f64(_bits(spec, name)[c0:c1, g:g + 1, :])
 
 
-def _fwd_task(spec, h, src, kpos, r0, r1):
+def _fwd_task(spec, h, src, r0, r1):
     g = h // spec["group"]
-    q, vis, blocks = _key_blocks(spec, h, src, r0, r1, kpos)
+    q, vis, blocks = _key_blocks(spec, h, src, r0, r1)
     o = np.zeros((r1 - r0, 1, q.shape[2]))
     lse = np.full((1, r1 - r0), -np.inf)
     for c0, c1 in blocks:
@@ -175,9 +177,9 @@ def _fwd_task(spec, h, src, kpos, r0, r1):
     return o[:, 0, :], lse[0]
 
 
-def _bwd_task(spec, h, src, kpos, r0, r1, lse_rows, delta_rows):
+def _bwd_task(spec, h, src, r0, r1, lse_rows, delta_rows):
     g = h // spec["group"]
-    q, vis, blocks = _key_blocks(spec, h, src, r0, r1, kpos)
+    q, vis, blocks = _key_blocks(spec, h, src, r0, r1)
     do = _f64(_bits(spec, "do")[r0:r1, h:h + 1, :])
     dq = np.zeros((r1 - r0, q.shape[2]))
     parts = []
@@ -208,7 +210,7 @@ class Forward:
         ex = pool(workers)
         spec = sh.spec()
         self.blocks = _row_blocks(sh.n, rows_per_task)
-        self.futs = {(h, t, b): ex.submit(_fwd_task, spec, h, s, sh.kpos[s], r0, r1)
+        self.futs = {(h, t, b): ex.submit(_fwd_task, spec, h, s, r0, r1)
                      for h in self.heads for t, s in enumerate(self.order)
                      for b, (r0, r1) in enumerate(self.blocks)}
 
@@ -258,7 +260,7 @@ class Backward:
         ex = pool(workers)
         spec = sh.spec()
         self.blocks = _row_blocks(sh.n, rows_per_task)
-        self.futs = {(j, t, b): ex.submit(_bwd_task, spec, h, s, sh.kpos[s], r0, r1, lse[j, r0:r1],
+        self.futs = {(j, t, b): ex.submit(_bwd_task, spec, h, s, r0, r1, lse[j, r0:r1],
                                           self.delta[j, r0:r1])
                      for j, h in enumerate(self.heads) for t, s in enumerate(self.order)
                      for b, (r0, r1) in enumerate(self.blocks)}

@@ -179,15 +179,16 @@ def test_dkdv_split_matches_oracle(name, S, R, hq, hkv, d, window, packed, rank)
 
 
 @pytest.mark.timeout(600)
-def test_llama3_8b_fwd_bwd_full_size():
-    """Llama-3-8B shape, rank 0's share of S=256K at CP=16 (local 16K), 16 ring steps
-    forward and backward on the GPU.  For the query heads of KV head 5 (a whole GQA
+@pytest.mark.parametrize("rank,kvh", [(0, 5), (15, 2)])
+def test_llama3_8b_fwd_bwd_full_size(rank, kvh):
+    """Llama-3-8B shape, one rank's share of S=256K at CP=16 (local 16K), 16 ring
+    steps forward and backward on the GPU (rank 0: the first and last chunks; rank
+    15: the two middle ones).  For the query heads of one KV head (a whole GQA
     group) every local row's O, LSE and dQ and every step's dK/dV of every key of
     the visiting block, against the float64 oracle, whose backward starts from its
     own O and LSE.  For all 32 heads, sampled rows of O, LSE and dQ."""
     from tests.gpu_common import GroupReference, gqa_heads
     w = inputs.WORKLOADS["llama3_8b_fwdbwd"]
-    rank, kvh = 0, 5
     heads = gqa_heads(kvh, w.hq, w.hkv)
     from context_long_attention_amd.ring import RankRing
     note(f"bwd {w.name} full size rank={rank} whole group of KV head {kvh}")

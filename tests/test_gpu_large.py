@@ -21,37 +21,56 @@ def _needs_gpu():
     cpattn.lib()
 
 
+def _protocol_rows(w, seed):
+    """The row sample of the Llama-3-405B protocol: in each of the two zigzag query
+    chunks, its first and last 256 rows and 1024 uniform rows (seeded)."""
+    rng = np.random.default_rng(seed)
+    c = w.chunk
+    rows = []
+    for base in (0, c):
+        rows += [np.arange(base, base + 256), np.arange(base + c - 256, base + c), base + rng.integers(0, c, 1024)]
+    return np.unique(np.concatenate(rows))
+
+
 @pytest.mark.timeout(900)
 def test_llama3_405b_forward_full_size_sampled():
     """Hq=128, Hkv=8 (G=16), D=128: rank 0's share of S=1M at CP=16 (local 64K), 16
-    ring steps of 64K-token KV blocks.  The final O/LSE and every step's partial
-    (O_t, LSE_t), recomputed with the non-merging step kernel, on sampled rows (the
-    chunk edges and 32 uniform rows; each row costs the oracle about a second)."""
+    ring steps of 64K-token KV blocks.  On the protocol's row sample (per query chunk
+    the first and last 256 rows and 1024 uniform rows), all 128 heads: the final
+    O/LSE of the bench's fused ring, and every step's partial (O_t, LSE_t) recomputed
+    with the non-merging step kernel, against the float64 oracle (evaluated in the
+    worker pool; each row sees every key it depends on)."""
     from context_long_attention_amd import cpattn
     from context_long_attention_amd.ring import RankRing
+    from tests import oracle_par
     w = inputs.WORKLOADS["llama3_405b_fwd"]
-    note(f"fwd {w.name} full size rank 0")
     inp = RankInputs(w, 0)
     ring = RankRing(w, 0)
     sched = ring.schedule()
-    o, lse, _ = ring.forward(inp.q, inp.kv_of_source, keep_steps=False)
-    torch.cuda.synchronize()
-    rows = sampled_rows(w.local, w.chunk, 32, 3)
-    q_rows = widen(inp.q_bits[rows])
-    ro, rl, rsteps = oracle.rank_forward(q_rows, inp.qpos[rows], inp.blocks(sched), None, w.scale)
-    assert_o_close(o[rows].cpu().numpy(), ro, "405B O sampled rows")
-    assert_lse_close(lse[:, rows].cpu().numpy(), rl, "405B LSE sampled rows")
-    assert not torch.isnan(o).any().item()
-    rows_dev = torch.from_numpy(rows).cuda()
-    o_t = torch.empty_like(o)
-    l_t = torch.empty_like(lse)
-    for t, (rot, rlt) in enumerate(rsteps):
-        k, v = inp.kv_of_source(sched[t])
-        cpattn.cp_attn_fwd_step(ring.problem(t), inp.q, k, v, o_t, l_t)
-        got_o = o_t.index_select(0, rows_dev).cpu().numpy()
-        got_l = l_t.index_select(1, rows_dev).cpu().numpy()
-        assert_lse_close(got_l, rlt, f"405B LSE_t step {t}")
-        assert_o_close(got_o, rot, f"405B O_t step {t}", np.isfinite(rlt).T)
+    rows = _protocol_rows(w, 3)
+    note(f"fwd {w.name} full size rank 0, {len(rows)} sampled rows")
+    with oracle_par.Shared(inp.q_bits[rows], inp.qpos[rows], {s: inp.kv_bits[s] for s in sched},
+                           {s: inp.kpos[s] for s in sched}, w.scale) as sh:
+        ref = oracle_par.Forward(sh, range(w.hq), sched, keep_steps=True)
+        o, lse, _ = ring.forward(inp.q, inp.kv_of_source, keep_steps=False)
+        torch.cuda.synchronize()
+        rows_dev = torch.from_numpy(rows).cuda()
+        got_o, got_l = o.index_select(0, rows_dev).cpu().numpy(), lse.index_select(1, rows_dev).cpu().numpy()
+        assert not torch.isnan(o).any().item()
+        o_t = torch.empty_like(o)
+        l_t = torch.empty_like(lse)
+        steps = []
+        for t in range(w.cp):
+            k, v = inp.kv_of_source(sched[t])
+            cpattn.cp_attn_fwd_step(ring.problem(t), inp.q, k, v, o_t, l_t)
+            steps.append((o_t.index_select(0, rows_dev).cpu().numpy(), l_t.index_select(1, rows_dev).cpu().numpy()))
+        del o, lse, o_t, l_t
+        ro, rl, rsteps = ref.result()
+    assert_o_close(got_o, ro, "405B O sampled rows")
+    assert_lse_close(got_l, rl, "405B LSE sampled rows")
+    for t, ((go, gl), (rot, rlt)) in enumerate(zip(steps, rsteps)):
+        assert_lse_close(gl, rlt, f"405B LSE_t step {t}")
+        assert_o_close(go, rot, f"405B O_t step {t}", np.isfinite(rlt).T)
 
 
 def _packed_setup():
