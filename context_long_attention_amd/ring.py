@@ -127,7 +127,7 @@ class RankRing:
 
     # ------------------------------------------------------------- forward
     def forward(self, q, kv_of_source, stage: bool = True, keep_steps: bool = False, schedule=None,
-                timer=None, fused: bool = True):
+                timer=None, fused: bool = True, start: int = 0, stop: int | None = None, state=None):
         """Run the rank's forward ring.
 
         q: device bf16 [2c, Hq, D]; kv_of_source(src) -> (k, v) device bf16 [2c, Hkv, D].
@@ -136,27 +136,51 @@ class RankRing:
         fused: step 0 writes the accumulator and later steps merge into it inside the
         kernel (cp_attn_fwd_step_merge); otherwise every step writes its partial and
         cp_merge_partials folds it in (always so when keep_steps asks for the partials).
+
+        start, stop, state: run only ring steps start .. stop - 1.  The merge is
+        associative ("Context Parallelism for Scalable Million-Token Inference",
+        section "Ring Attention Algorithms"), so the running (O, LSE) after any
+        step is a complete ring state: ``state`` = (O, LSE) device fp32 tensors
+        holding the merge of steps 0 .. start - 1 (required when start > 0) are
+        merged into in place and returned, and the ring continues as if it had
+        never stopped.
         """
         w = self.w
         rows = 2 * self.c
         sched = self.schedule() if schedule is None else list(schedule)
         check_schedule(self.R, sched)
+        stop = len(sched) if stop is None else stop
+        if not 0 <= start <= stop <= len(sched):
+            raise ValueError(f"ring steps {start} .. {stop - 1} outside 0 .. {len(sched) - 1}")
+        if (state is None) != (start == 0):
+            raise ValueError("a ring resumed after step 0 needs the (O, LSE) state of the steps before it, "
+                             "and one started at step 0 takes none")
         dev = self.device
         fused = fused and not keep_steps
         steps = []
         compute = torch.cuda.current_stream(dev)
-        if fused:
+        if state is not None:
+            o_acc, lse_acc = state
+            index = dev.index if dev.index is not None else torch.cuda.current_device()
+            if (tuple(o_acc.shape) != (rows, w.hq, w.dim) or tuple(lse_acc.shape) != (w.hq, rows)
+                    or o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32
+                    or not (o_acc.is_cuda and lse_acc.is_cuda)
+                    or o_acc.device.index != index or lse_acc.device.index != index
+                    or not o_acc.is_contiguous() or not lse_acc.is_contiguous()):
+                raise ValueError("ring state must be contiguous fp32 O [2c, Hq, D] and LSE [Hq, 2c] on the device")
+        elif fused:
             # the query segments cover every local row, so step 0 writes all of them
             o_acc = torch.empty((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
             lse_acc = torch.empty((w.hq, rows), dtype=torch.float32, device=dev)
         else:
             o_acc = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
             lse_acc = torch.full((w.hq, rows), float("-inf"), dtype=torch.float32, device=dev)
+        if not fused:
             o_t = torch.empty_like(o_acc)
             lse_t = torch.empty_like(lse_acc)
         # steps with no visible pair are neither received nor computed (their
         # partial is the merge identity); step 0 (the diagonal) is always live
-        live = [t for t in range(len(sched)) if keep_steps or t == 0 or self.source_live(sched[t])]
+        live = [t for t in range(start, stop) if keep_steps or t == 0 or self.source_live(sched[t])]
         feeder = _Feeder(kv_of_source, [sched[t] for t in live], stage, dev, local=self.rank)
         for i, t in enumerate(live):
             src = sched[t]
@@ -266,7 +290,8 @@ class _Feeder:
             self.ready = [torch.cuda.Event(), torch.cuda.Event()]
             self.free = [torch.cuda.Event(), torch.cuda.Event()]
             self.free_recorded = [False, False]
-            self._issue(0)
+            if self.sched:
+                self._issue(0)
 
     def _groups(self, src):
         return [(i,) for i in range(len(src))] if self.pack is None else self.pack

@@ -207,6 +207,67 @@ def test_fused_step_merge_from_arbitrary_state(d):
     assert np.array_equal(o_acc.cpu().numpy().transpose(1, 0, 2)[dead], o0.transpose(1, 0, 2)[dead])
 
 
+RESUME = [
+    ("tiny", None),
+    ("ragged", None),
+    ("packed", np.array([0, 1, 2, 130, 131, 300, 301, 520, 767, 768], dtype=np.int32)),
+]
+
+
+@pytest.mark.parametrize("case,cu", RESUME, ids=[r[0] for r in RESUME])
+def test_ring_resumes_from_a_host_copy_of_its_state(case, cu):
+    """A ring stopped after step k, its (O, LSE) state copied to host memory and
+    the device tensors freed, then resumed from a fresh device copy of that
+    state, ends bit-identical to the uninterrupted ring and matches the oracle,
+    for every k, on the fused and the separate-merge paths."""
+    w = {"tiny": inputs.WORKLOADS["tiny"],
+         "ragged": inputs.Workload("resume_ragged", 2 * 4 * 300, 4, 8, 2, 128, backward=False),
+         "packed": inputs.Workload("resume_packed", 768, 4, 8, 2, 128, backward=False, packed=True)}[case]
+    for rank in sorted({0, w.cp - 1}):
+        note(f"resume {w.name} rank={rank}")
+        inp = RankInputs(w, rank)
+        ring = _ring(w, rank, cu)
+        ro, rlse, _ = oracle.rank_forward(inp.q64, inp.qpos, _oracle_blocks(inp, ring), cu, w.scale)
+        live = np.isfinite(rlse).T
+        for fused in (True, False):
+            o_full, l_full, _ = ring.forward(inp.q, inp.kv_of_source, fused=fused)
+            torch.cuda.synchronize()
+            want_o, want_l = o_full.cpu().numpy(), l_full.cpu().numpy()
+            for k in range(1, w.cp):
+                o_k, l_k, _ = ring.forward(inp.q, inp.kv_of_source, fused=fused, stop=k)
+                host_o, host_l = o_k.cpu().numpy().copy(), l_k.cpu().numpy().copy()
+                del o_k, l_k
+                torch.cuda.synchronize()
+                state = (torch.from_numpy(host_o).cuda(), torch.from_numpy(host_l).cuda())
+                o, lse, _ = ring.forward(inp.q, inp.kv_of_source, fused=fused, start=k, state=state)
+                torch.cuda.synchronize()
+                assert o.data_ptr() == state[0].data_ptr() and lse.data_ptr() == state[1].data_ptr()
+                got_o, got_l = o.cpu().numpy(), lse.cpu().numpy()
+                assert np.array_equal(got_o, want_o), f"O after resuming at step {k} (fused={fused})"
+                assert np.array_equal(got_l, want_l), f"LSE after resuming at step {k} (fused={fused})"
+                assert_o_close(got_o, ro, f"resumed O rank {rank} k={k}", live)
+                assert_lse_close(got_l, rlse, f"resumed LSE rank {rank} k={k}")
+
+
+def test_ring_resume_rejects_a_missing_or_misshapen_state():
+    w = inputs.WORKLOADS["tiny"]
+    inp = RankInputs(w, 0)
+    ring = _ring(w, 0)
+    rows = 2 * w.chunk
+    good = (torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device="cuda"),
+            torch.full((w.hq, rows), float("-inf"), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        ring.forward(inp.q, inp.kv_of_source, start=1)
+    with pytest.raises(ValueError):
+        ring.forward(inp.q, inp.kv_of_source, state=good)
+    with pytest.raises(ValueError):
+        ring.forward(inp.q, inp.kv_of_source, start=1, state=(good[0][1:], good[1]))
+    with pytest.raises(ValueError):
+        ring.forward(inp.q, inp.kv_of_source, start=1, state=(good[0], good[1].double()))
+    with pytest.raises(ValueError):
+        ring.forward(inp.q, inp.kv_of_source, start=2, stop=1, state=good)
+
+
 def test_clock_probe_records_every_workgroup():
     """cp_debug_clock_probe: each workgroup of a launch records start/end cycle and
     100 MHz tick counters; the implied shader clock is a plausible one."""
