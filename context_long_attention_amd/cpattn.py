@@ -104,9 +104,14 @@ def _check(status: int):
 
 
 def _ptr(t):
-    """Device address of a torch tensor (None -> NULL)."""
+    """Device address of a torch tensor (None -> NULL).  The C ABI takes dense
+    row-major buffers, so a strided view (a transpose, a column slice) is refused
+    rather than passed on as if it were one."""
     if t is None:
         return None
+    if not t.is_contiguous():
+        raise ValueError(f"tensor of shape {tuple(t.shape)} and strides {tuple(t.stride())} is not contiguous; "
+                         "the C ABI takes dense row-major buffers")
     return ctypes.c_void_p(t.data_ptr())
 
 

@@ -439,3 +439,17 @@ def test_block_map_and_pairs_on_arbitrary_segments(prob):
         for _, kp, kl in ks:
             want += int(oracle.visibility(np.arange(qp, qp + ql), np.arange(kp, kp + kl), cu, window or None).sum())
     assert cpattn.cp_count_pairs(p) == want
+
+
+def test_binding_refuses_strided_tensors():
+    """The ABI takes dense row-major buffers: the binding passes a contiguous
+    tensor's address and refuses a transposed or column-sliced view, whose
+    data_ptr would be read with the wrong layout."""
+    torch = pytest.importorskip("torch")
+    a = torch.zeros((6, 4), dtype=torch.float32)
+    assert cpattn._ptr(a).value == a.data_ptr()
+    assert cpattn._ptr(a[2:5]).value == a[2:5].data_ptr()  # a run of rows stays dense
+    assert cpattn._ptr(None) is None
+    for bad in (a.t(), a[:, 1:3], torch.zeros((4, 6)).t().contiguous().t()):
+        with pytest.raises(ValueError, match="not contiguous"):
+            cpattn._ptr(bad)
