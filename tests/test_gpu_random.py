@@ -191,3 +191,53 @@ def test_random_cases_cover_every_feature():
     assert any(c["cu"] is not None for c in cs) and any(c["window"] for c in cs)
     assert any(n == 0 for c in cs for _, _, n in c["qsegs"] + c["ksegs"])
     assert {c["kv_split"] for c in cs} >= {0, 1, 2, 8} and {c["d"] for c in cs} == {64, 128}
+
+
+N_RINGS = 120
+
+
+def _ring_case(seed):
+    """A random ring: S = 2 R c tokens over R ranks, one rank's share, with or
+    without packed documents and a sliding window."""
+    from context_long_attention_amd import inputs
+    rng = np.random.default_rng(5000 + seed)
+    R = int(rng.integers(1, 9))
+    c = int(rng.choice([1, 2, 3, 17, 32, 63, 64, 65, 96, 129, 150]))
+    S = 2 * R * c
+    hq, hkv = HEADS[int(rng.integers(len(HEADS)))]
+    d = int(rng.choice([64, 128]))
+    cu = None
+    if rng.random() < 0.35:
+        cuts = np.unique(rng.integers(1, S, int(rng.integers(0, 12)))) if S > 1 else np.zeros(0, dtype=np.int64)
+        cu = np.concatenate([[0], cuts, [S]]).astype(np.int32)
+    window = int(rng.choice([0, 0, 1, max(1, c // 2 + 1), c, 2 * c + 1, S]))
+    w = inputs.Workload(f"ring{seed}", S, R, hq, hkv, d, backward=True, packed=cu is not None, window=window)
+    return w, int(rng.integers(0, R)), cu
+
+
+@pytest.mark.parametrize("case", range(N_RINGS))
+def test_random_ring_matches_oracle(case):
+    """One rank's whole forward and backward ring (RankRing: live-step skipping,
+    the receive double buffer, the fused merge, the library's dK/dV split and its
+    workspace) against the oracle's replay of the same ring."""
+    from context_long_attention_amd.ring import RankRing
+    from tests.gpu_common import RankInputs
+    w, rank, cu = _ring_case(case)
+    note(f"random ring {case}: S={w.seq_len} R={w.cp} c={w.chunk} Hq={w.hq} Hkv={w.hkv} D={w.dim} rank={rank} "
+         f"window={w.window} docs={None if cu is None else len(cu) - 1}")
+    inp = RankInputs(w, rank, want_do=True)
+    ring = RankRing(w, rank, cu)
+    o, lse, _ = ring.forward(inp.q, inp.kv_of_source)
+    dq, per_step = ring.backward(inp.q, inp.do, o, lse, inp.kv_of_source)
+    torch.cuda.synchronize()
+    blocks = [inp.kv64[s] for s in ring.schedule()]
+    win = w.window or None
+    ro, rl, _ = oracle.rank_forward(inp.q64, inp.qpos, blocks, cu, w.scale, window=win)
+    rdq, rsteps, _ = oracle.rank_backward(inp.q64, inp.qpos, inp.do64, ro, rl, blocks, cu, w.scale, window=win)
+    assert_o_close(o.cpu().numpy(), ro, f"ring {case}: O", np.isfinite(rl).T)
+    assert_lse_close(lse.cpu().numpy(), rl, f"ring {case}: LSE")
+    _grad_close(dq.cpu().numpy(), rdq, f"ring {case}: dQ")
+    for t, ((src, dk, dv), (rdk, rdv)) in enumerate(zip(per_step, rsteps)):
+        assert src == ring.schedule()[t]
+        _grad_close(dk.cpu().numpy(), rdk, f"ring {case}: dK step {t}")
+        _grad_close(dv.cpu().numpy(), rdv, f"ring {case}: dV step {t}")
