@@ -68,10 +68,12 @@ struct BwdParams {
     int32_t qs_row0[2], qs_pos0[2], qs_len[2];
     int32_t ks_row0[2], ks_pos0[2], ks_len[2];
     int32_t mask[2][2];
-    // dK/dV kernel: 128-key tiles, each spread over kv_split workgroups
-    int32_t ktiles0, n_ktiles, n_work_kv, kv_split;
-    // dQ kernel: query tiles of BMQ rows
-    int32_t qtiles0, n_qtiles, n_work_q, n_hb;
+    // dK/dV kernel: 128-key tiles, each spread over kv_split workgroups;
+    // k_last: key tiles latest first instead of earliest first
+    int32_t ktiles0, n_ktiles, n_work_kv, kv_split, k_last;
+    // dQ kernel: query tiles of BMQ rows; q_first: earliest first instead of
+    // latest first
+    int32_t qtiles0, n_qtiles, n_work_q, n_hb, q_first;
 };
 
 // ============================================================================ dK / dV
@@ -106,7 +108,7 @@ struct KvBlock {
 __device__ __forceinline__ KvBlock kv_block(const BwdParams& p, int b) {
     KvBlock k;
     k.g = b % p.hkv;
-    const int kt = b / p.hkv;
+    const int kt = p.k_last ? p.n_ktiles - 1 - b / p.hkv : b / p.hkv;
     k.s = (kt < p.ktiles0) ? 0 : 1;
     k.kt_in = k.s ? kt - p.ktiles0 : kt;
     k.key_row0 = p.ks_row0[k.s] + k.kt_in * BK;
@@ -190,7 +192,8 @@ __global__ __launch_bounds__(kKvThreads, 2) void bwd_dkdv_kernel(const BwdParams
 
     // workgroup w takes part w / n_work_kv of key block b = w mod n_work_kv, which
     // runs on XCD b mod 8 when n_work_kv is a multiple of 8 (workgroups are dealt
-    // round-robin): KV head b mod Hkv, key tiles earliest first (the most queries)
+    // round-robin): KV head b mod Hkv, key tiles earliest first (the most queries
+    // under a causal mask; latest first when the host found those to see more)
     const int w = blockIdx.x;
     if (w >= p.n_work_kv * p.kv_split) return;
     const int part = w / p.n_work_kv;
@@ -485,11 +488,12 @@ __global__ __launch_bounds__(kQThreads, 2) void bwd_dq_kernel(const BwdParams p)
     const int hl = lane >> 5;
     const int ql = lane & 31;
 
-    // as in the forward: head block w mod n_hb, query tiles latest first
+    // as in the forward: head block w mod n_hb, query tiles latest first (or
+    // earliest first where those see the most keys)
     const int w = blockIdx.x;
     if (w >= p.n_work_q) return;
     const int hb = w % p.n_hb;
-    const int qt = p.n_qtiles - 1 - w / p.n_hb;
+    const int qt = p.q_first ? w / p.n_hb : p.n_qtiles - 1 - w / p.n_hb;
     const int qs = (qt < p.qtiles0) ? 0 : 1;
     const int qt_in = qs ? qt - p.qtiles0 : qt;
     const int tile_row0 = p.qs_row0[qs] + qt_in * BMQ;
@@ -795,6 +799,7 @@ cp_status bwd_step(const cp_attn_problem* p, const void* q, const void* k, const
             prm.mask[i][j] = (i < p->n_q_seg && j < p->n_kv_seg) ? p->mask[i][j] : CP_MASK_SKIP;
     prm.ktiles0 = int32_t(ceil_div(prm.ks_len[0], BK));
     prm.n_ktiles = int32_t(nk);
+    prm.k_last = dkdv_latest_first(p) ? 1 : 0;
     const int64_t work_kv = nk * p->hkv;
     // dQ: query segments that see no KV segment get nothing and stay out of the
     // launch (the dK/dV kernel still walks every segment)
@@ -812,6 +817,12 @@ cp_status bwd_step(const cp_attn_problem* p, const void* q, const void* k, const
     prm_q.nq_seg = lq.n_q_seg;
     prm_q.qtiles0 = int32_t(ceil_div(prm_q.qs_len[0], gq.bm));
     prm_q.n_qtiles = int32_t(nq);
+    {
+        // the heaviest query tiles first (their work listed in the default order)
+        std::vector<int64_t> work = query_tile_work(&lq, gq.bm, kBN);
+        std::reverse(work.begin(), work.end());
+        prm_q.q_first = heavier_last(work) ? 1 : 0;
+    }
     const int64_t work_q = nq * (p->hq / gq.hpw);
     if (work_kv == 0 && work_q == 0) return CP_OK;
     if (!q || !k || !v || !d_o || !lse || !delta || !dq_acc || !dk_out || !dv_out)

@@ -31,8 +31,10 @@
 //    element mask runs only on partially visible or ragged tiles.
 //  * Work items are dealt to the XCDs round-robin: each XCD keeps the same head
 //    blocks (K/V shared in its L2; with Hkv a multiple of 8 all head blocks of
-//    a KV head share one XCD), latest query positions first, and query tiles of
-//    a head block shared by several XCDs interleave across them.
+//    a KV head share one XCD), the query tiles with the most keys first (latest
+//    positions, or earliest where a window's triangle makes those the longest),
+//    and query tiles of a head block shared by several XCDs interleave across
+//    them.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -78,6 +80,7 @@ struct FwdParams {
     int32_t qtiles0, n_qtiles;
     int32_t ktiles0, n_ktiles;
     int32_t n_work, n_hb;
+    int32_t q_first;          // query tiles earliest first instead of latest first
     unsigned long long* clk;  // diagnostics: per-workgroup start/end counters, or null
     int32_t clk_wgs;
 };
@@ -113,7 +116,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
     // ---- work decode.  Workgroups are dealt to the 8 XCDs round-robin by id, so
     // item w goes to XCD w mod 8: head block u = w mod n_hb (every XCD keeps the
     // same head blocks, whose K/V then stay in its L2) and query tiles latest
-    // first (the most keys), interleaved across the XCDs sharing a head block.
+    // first (the most keys under a causal mask; earliest first when the host
+    // found those to see more), interleaved across the XCDs sharing a head block.
     const int w = blockIdx.x;
     if (w >= p.n_work) return;
     const bool probe = p.clk != nullptr && w < p.clk_wgs;
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_step_kernel(const FwdParams p
         const int nb = p.n_hb / p.hkv;  // head blocks per KV head
         hb = ((u & 7) + 8 * ((u >> 3) / nb)) * nb + (u >> 3) % nb;
     }
-    const int qt = p.n_qtiles - 1 - w / p.n_hb;
+    const int qt = p.q_first ? w / p.n_hb : p.n_qtiles - 1 - w / p.n_hb;
     const int qs = (qt < p.qtiles0) ? 0 : 1;
     const int qt_in = qs ? qt - p.qtiles0 : qt;
     // Segment parameters as opaque scalars; nothing below indexes the parameter
@@ -669,6 +673,12 @@ cp_status fwd_step(const cp_attn_problem* p, const void* q, const void* k, const
     if (!kv_spans_fit(p)) return fail(CP_ERR_UNSUPPORTED, "a KV segment spans 1 GiB or more");
     prm.n_work = int32_t(n_work);
     prm.n_hb = p->hq / g.hpw;
+    {
+        // the heaviest query tiles first (their work listed in the default order)
+        std::vector<int64_t> work = query_tile_work(p, g.bm, g.bn);
+        std::reverse(work.begin(), work.end());
+        prm.q_first = heavier_last(work) ? 1 : 0;
+    }
     const int grid = int(n_work);
     hipError_t e;
     if (p->head_dim == 128) {

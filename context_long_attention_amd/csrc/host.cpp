@@ -114,17 +114,52 @@ int64_t row_lower_bound(const cp_attn_problem* p, int mask, int64_t q) {
     return lo;
 }
 
-int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_cu) {
-    // Per 128-key block: the query tiles (of kBwdQRows rows, per query head) that
-    // see one of its keys, by the ranges the dK/dV kernel walks.  With documents
-    // and no host cu_seqlens the ranges are unknown: no split.
-    bool any_doc = false;
+static bool any_doc_pair(const cp_attn_problem* p) {
     for (int i = 0; i < p->n_q_seg; ++i)
-        for (int j = 0; j < p->n_kv_seg; ++j) any_doc |= (p->mask[i][j] == CP_MASK_DOC);
-    if (any_doc && !host_cu) return 1;
+        for (int j = 0; j < p->n_kv_seg; ++j)
+            if (p->mask[i][j] == CP_MASK_DOC) return true;
+    return false;
+}
+
+bool heavier_last(const std::vector<int64_t>& work) {
+    const int64_t n = int64_t(work.size());
+    double total = 0.0, moment = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        total += double(work[size_t(i)]);
+        moment += double(i) * double(work[size_t(i)]);
+    }
+    if (n < 2 || total <= 0.0) return false;
+    return moment / total > 0.5 * double(n - 1) + 0.01 * double(n - 1);
+}
+
+std::vector<int64_t> query_tile_work(const cp_attn_problem* p, int bm, int bn) {
+    std::vector<int64_t> work;
+    if (any_doc_pair(p)) return work;
+    for (int i = 0; i < p->n_q_seg; ++i) {
+        const cp_segment& qs = p->q_seg[i];
+        for (int64_t qt = 0; qt < ceil_div(qs.len, bm); ++qt) {
+            const int64_t q0 = qs.pos0 + qt * bm;
+            const int64_t q1 = std::min(qs.pos0 + qs.len, q0 + bm) - 1;
+            int64_t n = 0;
+            for (int j = 0; j < p->n_kv_seg; ++j) {
+                const int m = p->mask[i][j];
+                const TileRange r = tile_range(m, q0, q1, row_lower_bound(p, m, q0), p->kv_seg[j].pos0,
+                                               p->kv_seg[j].len, bn);
+                n += r.t_hi - r.t_lo;
+            }
+            work.push_back(n);
+        }
+    }
+    return work;
+}
+
+std::vector<int64_t> key_block_items(const cp_attn_problem* p, const int32_t* host_cu) {
+    // Per 128-key block: the query tiles (of kBwdQRows rows, per query head) that
+    // see one of its keys, by the ranges the dK/dV kernel walks.
+    std::vector<int64_t> items;
+    if (any_doc_pair(p) && !host_cu) return items;
     constexpr int64_t kInf = std::numeric_limits<int64_t>::max();
     const int64_t group = p->hq / p->hkv;
-    std::vector<int64_t> items;  // per block, in the kernel's key-tile order
     for (int j = 0; j < p->n_kv_seg; ++j) {
         const cp_segment& ks = p->kv_seg[j];
         for (int64_t kb = 0; kb < ceil_div(ks.len, kBwdKeysPerWG); ++kb) {
@@ -163,6 +198,20 @@ int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_c
             items.push_back(n * group);
         }
     }
+    return items;
+}
+
+bool dkdv_latest_first(const cp_attn_problem* p) {
+    return !any_doc_pair(p) && heavier_last(key_block_items(p, nullptr));
+}
+
+int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_cu) {
+    // With documents and no host cu_seqlens the blocks' ranges are unknown: no split.
+    if (any_doc_pair(p) && !host_cu) return 1;
+    const std::vector<int64_t> items = key_block_items(p, host_cu);  // per block, in key-tile index order
+    // the launch's block order, as the kernel takes it (documents: earliest first)
+    const bool latest_first = !any_doc_pair(p) && heavier_last(items);
+    const int64_t n_kt = int64_t(items.size());
     // Makespan of the launch in item times when workgroup w starts on the first
     // free slot in id order (two dK/dV workgroups per CU): part w / n_blocks of
     // block w mod n_blocks, whose key blocks run KV-head-minor, with the items of
@@ -178,7 +227,8 @@ int32_t dkdv_split(const cp_attn_problem* p, const int32_t* host_cu, int64_t n_c
         std::priority_queue<double, std::vector<double>, std::greater<double>> free_at;
         double end = 0.0;
         for (int64_t w = 0; w < split * n_blocks; ++w) {
-            const int64_t part = w / n_blocks, kt = (w % n_blocks) / p->hkv;
+            const int64_t part = w / n_blocks, kt0 = (w % n_blocks) / p->hkv;
+            const int64_t kt = latest_first ? n_kt - 1 - kt0 : kt0;
             const int64_t n = items[kt];
             const int64_t run = (n + split - 1) / split;
             const int64_t it0 = std::min(n, part * run);

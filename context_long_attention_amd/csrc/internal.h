@@ -5,6 +5,7 @@
 #include <cstdint>
 #include <initializer_list>
 #include <string>
+#include <vector>
 
 #include "cpattn.h"
 
@@ -83,6 +84,30 @@ int64_t doc_start_host(const int32_t* cu, int32_t n_docs, int64_t pos);
 // document start (DOC) and q - window + 1 (sliding window, DIAG_CAUSAL and DOC),
 // whichever is later; unbounded below otherwise.  Non-decreasing in q and <= q.
 int64_t row_lower_bound(const cp_attn_problem* p, int mask, int64_t q);
+
+// Work-item order.  The forward and dQ kernels take query tiles latest first
+// and the dK/dV kernel takes key blocks earliest first: under a causal mask
+// those have the most pairs, so the longest items start first.  Where the work
+// runs the other way (a sliding window's triangle at a chunk boundary, where
+// the earliest queries and the latest keys see the most), a launch takes its
+// items in the opposite order.  Decided on the host from every item's work;
+// problems with a DOC pair keep the default order (their ranges need the
+// documents, which a step call only has on the device).
+//
+// True when `work`, listed in a launch's default order, is heavier in its
+// second half (its centre of mass lies more than 1% of the span past the
+// middle), i.e. when the launch should take its items from the other end.
+bool heavier_last(const std::vector<int64_t>& work);
+// Visible key tiles (bn keys each) of every query tile (bm rows each) of the
+// forward and dQ kernels, in tile index order (first query segment first).
+// Empty when a pair is DOC.
+std::vector<int64_t> query_tile_work(const cp_attn_problem* p, int bm, int bn);
+// Query items (kBwdQRows rows of one query head) of every 128-key block of
+// one KV head, in the dK/dV kernel's key-tile index order.  host_cu: host
+// cu_seqlens for DOC pairs; empty with a DOC pair and no host_cu.
+std::vector<int64_t> key_block_items(const cp_attn_problem* p, const int32_t* host_cu);
+// The dK/dV launch order: key blocks latest first instead of earliest first.
+bool dkdv_latest_first(const cp_attn_problem* p);
 
 // Number of workgroups (1..kMaxKvSplit) over which the dK/dV kernel spreads
 // each key block's query items: the one with the shortest simulated launch,
