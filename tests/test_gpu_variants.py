@@ -79,10 +79,13 @@ def test_pass_q_packed_documents():
 @pytest.mark.parametrize("P,N,R,d", [(768, 512, 2, 128), (384, 768, 3, 64), (0, 512, 2, 128)])
 def test_partial_prefill(P, N, R, d):
     """New tokens against the cached prefix and each other over the ring."""
+    _partial_prefill(P, N, R, 8, 2, d)
+
+
+def _partial_prefill(P, N, R, hq, hkv, d):
     from context_long_attention_amd.variants import PartialPrefillRank
-    hq, hkv = 8, 2
     S = P + N
-    note(f"partial prefill P={P} N={N} R={R} D={d}")
+    note(f"partial prefill P={P} N={N} R={R} Hq={hq} Hkv={hkv} D={d}")
     q64, _ = device_bf16(inputs.chunk_normal(21, 0, S, hq, d))
     k64, _ = device_bf16(inputs.chunk_normal(22, 0, S, hkv, d))
     v64, _ = device_bf16(inputs.chunk_normal(23, 0, S, hkv, d))
@@ -99,6 +102,44 @@ def test_partial_prefill(P, N, R, d):
         ro, rl = ov.partial_prefill_rank(q64[new_r], new_r, blocks, d ** -0.5)
         assert_o_close(o.cpu().numpy(), ro, f"partial prefill O rank {r}")
         assert_lse_close(lse.cpu().numpy(), rl, f"partial prefill LSE rank {r}")
+
+
+N_RANDOM = 24
+RANDOM_HEADS = [(4, 1), (8, 2), (6, 2), (16, 4), (6, 3), (8, 8), (2, 1)]
+
+
+def _random_pass_q(seed):
+    rng = np.random.default_rng(7000 + seed)
+    R = int(rng.integers(1, 7))
+    c = int(rng.choice([1, 2, 17, 63, 64, 65, 100]))
+    hq, hkv = RANDOM_HEADS[int(rng.integers(len(RANDOM_HEADS)))]
+    w = inputs.Workload(f"pq_random{seed}", 2 * R * c, R, hq, hkv, int(rng.choice([64, 128])), backward=False)
+    cu = None
+    if rng.random() < 0.4:
+        cuts = np.unique(rng.integers(1, w.seq_len, int(rng.integers(0, 8)))) if w.seq_len > 1 else []
+        cu = np.concatenate([[0], cuts, [w.seq_len]]).astype(np.int32)
+    return w, cu
+
+
+@pytest.mark.parametrize("case", range(N_RANDOM))
+def test_pass_q_random(case):
+    """Seeded random Pass-Q rings (R = 1-6, chunks of 1-100 tokens, G = 1-8,
+    D = 64/128, random documents): every rank's partials and every owner's
+    restored output against the oracle."""
+    w, cu = _random_pass_q(case)
+    _pass_q_all_ranks(w, cu)
+
+
+@pytest.mark.parametrize("case", range(N_RANDOM))
+def test_partial_prefill_random(case):
+    """Seeded random partial prefills: cached prefix and new tokens of any size
+    that splits into 2R chunks (an empty prefix included), R = 1-5."""
+    rng = np.random.default_rng(8000 + case)
+    R = int(rng.integers(1, 6))
+    P = 2 * R * int(rng.choice([0, 1, 7, 32, 65]))
+    N = 2 * R * int(rng.choice([1, 3, 32, 64, 97]))
+    hq, hkv = RANDOM_HEADS[int(rng.integers(len(RANDOM_HEADS)))]
+    _partial_prefill(P, N, R, hq, hkv, int(rng.choice([64, 128])))
 
 
 @pytest.mark.parametrize("docs", [False, True])
