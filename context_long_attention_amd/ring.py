@@ -149,25 +149,15 @@ class RankRing:
         rows = 2 * self.c
         sched = self.schedule() if schedule is None else list(schedule)
         check_schedule(self.R, sched)
-        stop = len(sched) if stop is None else stop
-        if not 0 <= start <= stop <= len(sched):
-            raise ValueError(f"ring steps {start} .. {stop - 1} outside 0 .. {len(sched) - 1}")
-        if (state is None) != (start == 0):
-            raise ValueError("a ring resumed after step 0 needs the (O, LSE) state of the steps before it, "
-                             "and one started at step 0 takes none")
+        stop = _step_range(start, stop, len(sched), state, "(O, LSE)")
         dev = self.device
         fused = fused and not keep_steps
         steps = []
         compute = torch.cuda.current_stream(dev)
         if state is not None:
             o_acc, lse_acc = state
-            index = dev.index if dev.index is not None else torch.cuda.current_device()
-            if (tuple(o_acc.shape) != (rows, w.hq, w.dim) or tuple(lse_acc.shape) != (w.hq, rows)
-                    or o_acc.dtype != torch.float32 or lse_acc.dtype != torch.float32
-                    or not (o_acc.is_cuda and lse_acc.is_cuda)
-                    or o_acc.device.index != index or lse_acc.device.index != index
-                    or not o_acc.is_contiguous() or not lse_acc.is_contiguous()):
-                raise ValueError("ring state must be contiguous fp32 O [2c, Hq, D] and LSE [Hq, 2c] on the device")
+            _check_state(o_acc, (rows, w.hq, w.dim), dev, "O")
+            _check_state(lse_acc, (w.hq, rows), dev, "LSE")
         elif fused:
             # the query segments cover every local row, so step 0 writes all of them
             o_acc = torch.empty((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
@@ -205,28 +195,40 @@ class RankRing:
 
     # ------------------------------------------------------------- backward
     def backward(self, q, d_o, o, lse, kv_of_source, stage: bool = True, schedule=None, keep_steps=True,
-                 timer=None):
+                 timer=None, start: int = 0, stop: int | None = None, state=None):
         """Run the rank's backward ring from the final O and LSE.
 
         Returns (dQ fp32 [2c, Hq, D], per-step list of (source, dK_t, dV_t) fp32 [2c, Hkv, D]).
         With keep_steps=False only the last step's dK/dV buffers are kept (benchmarking).
+
+        start, stop, state: run only ring steps start .. stop - 1, as in forward.
+        ``state`` is the dQ accumulator (device fp32 [2c, Hq, D]) summed over steps
+        0 .. start - 1 (required when start > 0); it is added to in place and
+        returned, and the per-step list covers the steps run.  Delta is recomputed
+        from the final O and dO on every call (the same bits each time).
         """
         w = self.w
         rows = 2 * self.c
         sched = self.schedule() if schedule is None else list(schedule)
         check_schedule(self.R, sched)
+        stop = _step_range(start, stop, len(sched), state, "dQ")
         dev = self.device
         compute = torch.cuda.current_stream(dev)
         delta = torch.empty((w.hq, rows), dtype=torch.float32, device=dev)
         cpattn.cp_attn_bwd_prep(d_o, o, delta, rows, w.hq, w.dim, stream=compute)
-        dq = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
+        if state is not None:
+            _check_state(state, (rows, w.hq, w.dim), dev, "dQ")
+            dq = state
+        else:
+            dq = torch.zeros((rows, w.hq, w.dim), dtype=torch.float32, device=dev)
         out = []
         # as in the forward: steps with no visible pair are skipped (their dK/dV
         # are zero; with keep_steps they are returned as zeros)
-        live = [t for t in range(len(sched)) if t == 0 or self.source_live(sched[t])]
+        live = [t for t in range(start, stop) if t == 0 or self.source_live(sched[t])]
         feeder = _Feeder(kv_of_source, [sched[t] for t in live], stage, dev, local=self.rank)
         dk = dv = None
-        for t, src in enumerate(sched):
+        for t in range(start, stop):
+            src = sched[t]
             if t not in live:
                 if keep_steps:
                     z = torch.zeros((rows, w.hkv, w.dim), dtype=torch.float32, device=dev)
@@ -248,6 +250,26 @@ class RankRing:
             feeder.release(i, compute)
             out.append((src, dk, dv))
         return dq, out
+
+
+def _step_range(start, stop, n, state, what):
+    """The end of a ring run over steps start .. stop - 1 (stop None: to the end),
+    checked against the schedule's length and the resume state."""
+    stop = n if stop is None else stop
+    if not 0 <= start <= stop <= n:
+        raise ValueError(f"ring steps {start} .. {stop - 1} outside 0 .. {n - 1}")
+    if (state is None) != (start == 0):
+        raise ValueError(f"a ring resumed after step 0 needs the {what} state of the steps before it, "
+                         "and one started at step 0 takes none")
+    return stop
+
+
+def _check_state(x, shape, dev, what):
+    """A resume state tensor must be contiguous fp32 of the accumulator's shape on the ring's device."""
+    index = dev.index if dev.index is not None else torch.cuda.current_device()
+    if (tuple(x.shape) != tuple(shape) or x.dtype != torch.float32 or not x.is_cuda or x.device.index != index
+            or not x.is_contiguous()):
+        raise ValueError(f"ring state {what} must be a contiguous fp32 tensor of shape {tuple(shape)} on the device")
 
 
 _SIDE_STREAMS = {}
