@@ -24,7 +24,10 @@ legs, 3 of the Llama-3-405B leg -- and the headline and training legs also give
 the median launch time of every ring step.  ``value`` itself is the whole-job
 rate over the K bracketed headline steps.  The float64 oracle is timed on the
 host on a bounded sample of the headline workload (``cpu_baseline``) and, with
-its rate extrapolated to the whole share, of the Llama-3-405B one.
+its rate extrapolated to the whole share, of the Llama-3-405B one; on the
+headline sample its result is also compared with the final O and LSE of the
+last measured ring (``cpu_baseline.parity``: max-abs error of O, max relative
+error of LSE, against the 2e-2 and 1e-3 bars).
 """
 from __future__ import annotations
 
@@ -157,9 +160,11 @@ def blas_threads():
         return len(os.sched_getaffinity(0))
 
 
-def cpu_baseline(w, rank, heads):
+def cpu_baseline(w, rank, heads, final=None):
     """The float64 oracle on a bounded sample: ``heads`` query heads of the GQA group
-    of KV head 0, every ring step of the rank, every local row."""
+    of KV head 0, every ring step of the rank, every local row.  ``final`` (the
+    GPU's final O and LSE of the same ring, optional): its errors against the
+    oracle on that sample are reported too."""
     import oracle
     from context_long_attention_amd import inputs
     threads = blas_threads()
@@ -178,12 +183,25 @@ def cpu_baseline(w, rank, heads):
     for k, v, kpos in blocks:
         flops += oracle.causal_flops(qpos, kpos, heads, w.dim)
     t0 = time.perf_counter()
-    oracle.rank_forward(q, qpos, blocks, None, w.scale)
+    ro, rl, _ = oracle.rank_forward(q, qpos, blocks, None, w.scale)
     dt = time.perf_counter() - t0
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{w.name} rank {rank}: forward of {heads} of {w.hq} query heads (KV head 0), "
-                      f"all {R} ring steps, all {2 * c} local rows, float64 NumPy; {dt:.1f} s",
-            "seconds": dt, "flops": flops}
+    out = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{w.name} rank {rank}: forward of {heads} of {w.hq} query heads (KV head 0), "
+                     f"all {R} ring steps, all {2 * c} local rows, float64 NumPy; {dt:.1f} s",
+           "seconds": dt, "flops": flops}
+    if final is not None:
+        go = final[0][:, :heads].cpu().numpy().astype(np.float64)
+        gl = final[1][:heads].cpu().numpy().astype(np.float64)
+        live = np.isfinite(rl).T
+        err_o = float(np.abs(go - ro)[live].max())
+        dead = np.isneginf(rl)
+        err_l = float((np.abs(gl[~dead] - rl[~dead]) / np.maximum(1.0, np.abs(rl[~dead]))).max())
+        out["parity"] = {"checked": f"final O and LSE of the last measured ring against the oracle on this sample "
+                                    f"({2 * c} rows x {heads} heads)",
+                         "o_max_abs_err": err_o, "lse_max_rel_err": err_l, "o_bar": 2e-2, "lse_bar": 1e-3,
+                         "same_minus_inf_rows": bool(np.array_equal(np.isneginf(gl), dead)),
+                         "within_bar": bool(err_o <= 2e-2 and err_l <= 1e-3 and np.array_equal(np.isneginf(gl), dead))}
+    return out
 
 
 def cpu_baseline_extrapolated(w, rank, row_stride=4, steps=(0, 1)):
@@ -280,10 +298,13 @@ def measure(torch, w, rank, steps, warmup, backward):
         fwd_timer(step, what, stream)
         bwd_timer(step, what, stream)
 
+    last = {}
+
     def one_step():
         # the host part of the path (partition, per-step classes) is redone every step
         r = RankRing(w, rank)
         o, lse, _ = r.forward(q, kv_of, stage=True, timer=timer)
+        last["o"], last["lse"] = o, lse  # the final output of the last pass (kept for the parity check)
         if backward:
             r.backward(q, d_o, o, lse, kv_of, stage=True, keep_steps=False, timer=timer)
 
@@ -321,6 +342,7 @@ def measure(torch, w, rank, steps, warmup, backward):
            "merge_avg_launch_ms": sum(merge_ms) / max(1, len(merge_ms)),
            "merge_bytes_per_launch": sum(fwd_algorithmic_bytes(w, live_rows(w, rank, t), True)
                                          for t in range(1, w.cp)) / max(1, w.cp - 1)}
+    out["final"] = (last["o"], last["lse"])
     if backward:
         out["bwd_kernel_ms"] = bwd_timer.total_ms() / steps
         out["bwd_step_ms"] = np.median(np.asarray(bwd_timer.launch_ms()).reshape(steps, w.cp), axis=0).tolist()
@@ -678,7 +700,7 @@ def main():
         record["gemm_reference"]["attention_over_gemm"] = round(value / record["gemm_reference"]["tflops"], 3)
     if not args.no_cpu_baseline:
         log("timing the float64 oracle on the host (cpu_baseline)")
-        record["cpu_baseline"] = cpu_baseline(w, args.rank, args.cpu_heads)
+        record["cpu_baseline"] = cpu_baseline(w, args.rank, args.cpu_heads, fwd["final"])
     print(json.dumps(record), flush=True)
 
 
