@@ -43,7 +43,7 @@ import oracle
 from context_long_attention_amd import inputs
 
 _POOL = None
-_MAX_WORKERS = 16  # the GPU machine's CPU share for one GPU
+_MAX_WORKERS = 16  # host CPU cores set aside beside one GPU
 _KEY_BLOCK = 2048  # keys per oracle call inside a task
 
 
