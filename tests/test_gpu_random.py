@@ -139,6 +139,19 @@ def test_random_problem_matches_oracle(case):
     assert np.all(go[qrows][~live[qrows]] == 0), f"case {case}: rows with no visible key must hold O = 0"
     assert_lse_close(gl[:, qrows], rl[:, qrows], f"case {case}: LSE")
     assert np.all(go[out_q] == SENTINEL) and np.all(gl[:, out_q] == SENTINEL), f"case {case}: rows outside written"
+    # the tile classes the kernel used equal the host's block map of the same problem
+    ph = cpattn.make_problem(hq, hkv, d, d ** -0.5, nq, nk, c["qsegs"], c["ksegs"], c["masks"],
+                             None if c["cu"] is None else c["cu"].ctypes.data,
+                             0 if c["cu"] is None else len(c["cu"]) - 1, c["window"], c["kv_split"])
+    n_qt, n_kt = cpattn.cp_block_map_size(ph)
+    if n_qt * n_kt:
+        tm = torch.full((n_qt, n_kt), 255, dtype=torch.uint8, device="cuda")
+        o2 = torch.empty_like(o)
+        l2 = torch.empty_like(lse)
+        cpattn.cp_attn_fwd_step(p, q, k, v, o2, l2, tile_map=tm)
+        torch.cuda.synchronize()
+        assert np.array_equal(tm.cpu().numpy(), cpattn.cp_block_map(ph)), f"case {case}: kernel block map"
+        assert np.array_equal(o2.cpu().numpy()[qrows], go[qrows]), f"case {case}: O with the block map asked for"
 
     # fused merge into a random valid state: rows that see nothing keep it bit for bit
     o0 = rng.standard_normal((nq, hq, d)).astype(np.float32)
