@@ -233,6 +233,18 @@ def test_schedule_check_rejects_dropped_or_repeated_steps():
         ring.forward(None, None, schedule=[1, 0, 0, 2])
 
 
+def test_ring_resume_arguments_checked_before_any_launch():
+    """A resumed ring needs the state of the steps before it and a step range
+    inside the schedule; both rings refuse otherwise before touching a device."""
+    w = inputs.WORKLOADS["tiny"]
+    ring = RankRing(w, 2, device="cpu")
+    for run in (lambda **kw: ring.forward(None, None, **kw), lambda **kw: ring.backward(None, None, None, None, None, **kw)):
+        for kw in (dict(start=1), dict(start=0, state=object()), dict(start=3, stop=2, state=object()),
+                   dict(start=0, stop=5), dict(start=-1, state=object())):
+            with pytest.raises(ValueError):
+                run(**kw)
+
+
 # ------------------------------------------------------------------ sliding window
 @pytest.mark.parametrize("S,R", [(16, 2), (48, 3), (64, 4), (80, 5), (512, 4)])
 def test_window_step_masks_match_brute_force(S, R):
