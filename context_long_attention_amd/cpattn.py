@@ -115,6 +115,23 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr())
 
 
+def _dev(t, elem_bytes, n_elems, what):
+    """Address of a device buffer that must hold at least ``n_elems`` elements of
+    ``elem_bytes`` bytes (the layout the C ABI reads or writes for this call).
+    The ABI receives bare pointers and cannot see sizes, so a tensor that is too
+    small, of the wrong element size or not on the GPU is refused here rather
+    than read or written out of bounds.  None passes through as NULL."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{what}: a device (GPU) tensor is required")
+    if t.element_size() != elem_bytes:
+        raise ValueError(f"{what}: {elem_bytes}-byte elements expected, got {t.element_size()}-byte {t.dtype}")
+    if t.numel() < n_elems:
+        raise ValueError(f"{what}: needs at least {n_elems} elements, got {t.numel()} (shape {tuple(t.shape)})")
+    return _ptr(t)
+
+
 def _stream(stream):
     if stream is None:
         import torch
@@ -220,13 +237,25 @@ def cp_count_pairs(p: cp_attn_problem) -> int:
 
 
 # ---------------------------------------------------------------- device calls
+def _fwd_args(p, q, k, v, o, lse, tile_map):
+    nq, nk = p.q_rows * p.hq * p.head_dim, p.kv_rows * p.hkv * p.head_dim
+    tm = None
+    if tile_map is not None:
+        a, b = cp_block_map_size(p)
+        tm = _dev(tile_map, 1, a * b, "tile_map")
+    return (_dev(q, 2, nq, "q"), _dev(k, 2, nk, "k"), _dev(v, 2, nk, "v"), _dev(o, 4, nq, "o"),
+            _dev(lse, 4, p.hq * p.q_rows, "lse"), tm)
+
+
 def cp_attn_fwd_step(p: cp_attn_problem, q, k, v, o_step, lse_step, tile_map=None, stream=None):
-    _check(lib().cp_attn_fwd_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_step), _ptr(lse_step),
-                                  _ptr(tile_map), _stream(stream)))
+    _check(lib().cp_attn_fwd_step(ctypes.byref(p), *_fwd_args(p, q, k, v, o_step, lse_step, tile_map),
+                                  _stream(stream)))
 
 
 def cp_merge_partials(o_acc, lse_acc, o_step, lse_step, rows, heads, head_dim, stream=None):
-    _check(lib().cp_merge_partials(_ptr(o_acc), _ptr(lse_acc), _ptr(o_step), _ptr(lse_step), rows, heads,
+    no, nl = rows * heads * head_dim, heads * rows
+    _check(lib().cp_merge_partials(_dev(o_acc, 4, no, "o_acc"), _dev(lse_acc, 4, nl, "lse_acc"),
+                                   _dev(o_step, 4, no, "o_step"), _dev(lse_step, 4, nl, "lse_step"), rows, heads,
                                    head_dim, _stream(stream)))
 
 
@@ -235,36 +264,48 @@ def cp_merge_partials_n(o_out, lse_out, o_parts, lse_parts, rows, heads, head_di
     n = len(o_parts)
     if len(lse_parts) != n:
         raise ValueError("o_parts and lse_parts differ in length")
-    op = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in o_parts])
-    lp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in lse_parts])
-    _check(lib().cp_merge_partials_n(_ptr(o_out), _ptr(lse_out), op, lp, n, rows, heads, head_dim, _stream(stream)))
+    no, nl = rows * heads * head_dim, heads * rows
+    op = (ctypes.c_void_p * max(n, 1))(*[_dev(t, 4, no, f"o_parts[{i}]") for i, t in enumerate(o_parts)])
+    lp = (ctypes.c_void_p * max(n, 1))(*[_dev(t, 4, nl, f"lse_parts[{i}]") for i, t in enumerate(lse_parts)])
+    _check(lib().cp_merge_partials_n(_dev(o_out, 4, no, "o_out"), _dev(lse_out, 4, nl, "lse_out"), op, lp, n, rows,
+                                     heads, head_dim, _stream(stream)))
 
 
 def cp_attn_fwd_step_merge(p: cp_attn_problem, q, k, v, o_acc, lse_acc, tile_map=None, stream=None):
-    _check(lib().cp_attn_fwd_step_merge(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o_acc), _ptr(lse_acc),
-                                        _ptr(tile_map), _stream(stream)))
+    _check(lib().cp_attn_fwd_step_merge(ctypes.byref(p), *_fwd_args(p, q, k, v, o_acc, lse_acc, tile_map),
+                                        _stream(stream)))
 
 
 def cp_debug_clock_probe(buf=None):
     """Record per-workgroup (cycles, 100 MHz ticks) at start and end of every forward
     step launch into ``buf`` (device int64 tensor, 4 values per workgroup); None stops."""
-    _check(lib().cp_debug_clock_probe(_ptr(buf), 0 if buf is None else buf.numel()))
+    _check(lib().cp_debug_clock_probe(_dev(buf, 8, 0, "buf"), 0 if buf is None else buf.numel()))
 
 
 def cp_attn_bwd_prep(d_o, o, delta, rows, heads, head_dim, stream=None):
-    _check(lib().cp_attn_bwd_prep(_ptr(d_o), _ptr(o), _ptr(delta), rows, heads, head_dim, _stream(stream)))
+    n = rows * heads * head_dim
+    _check(lib().cp_attn_bwd_prep(_dev(d_o, 2, n, "d_o"), _dev(o, 4, n, "o"), _dev(delta, 4, heads * rows, "delta"),
+                                  rows, heads, head_dim, _stream(stream)))
+
+
+def _bwd_args(p, q, k, v, d_o, lse, delta, dq, dk, dv):
+    nq, nk, nl = p.q_rows * p.hq * p.head_dim, p.kv_rows * p.hkv * p.head_dim, p.hq * p.q_rows
+    return (_dev(q, 2, nq, "q"), _dev(k, 2, nk, "k"), _dev(v, 2, nk, "v"), _dev(d_o, 2, nq, "d_o"),
+            _dev(lse, 4, nl, "lse"), _dev(delta, 4, nl, "delta"), _dev(dq, 4, nq, "dq_acc"),
+            _dev(dk, 4, nk, "dk_out"), _dev(dv, 4, nk, "dv_out"))
 
 
 def cp_attn_bwd_step(p: cp_attn_problem, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out, workspace=None,
                      stream=None):
     """workspace: a device tensor (any dtype) whose bytes serve the dK/dV split, or None."""
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib().cp_attn_bwd_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(lse), _ptr(delta),
-                                  _ptr(dq_acc), _ptr(dk_out), _ptr(dv_out), _ptr(workspace), ws_bytes,
-                                  _stream(stream)))
+    ws = None if workspace is None else _dev(workspace, workspace.element_size(), 0, "workspace")
+    _check(lib().cp_attn_bwd_step(ctypes.byref(p), *_bwd_args(p, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out),
+                                  ws, ws_bytes, _stream(stream)))
 
 
 def cp_attn_bwd_step_noalloc(p: cp_attn_problem, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out, stream=None):
     """cp_attn_bwd_step with the library's fixed per-device scratch as the workspace."""
-    _check(lib().cp_attn_bwd_step_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(d_o), _ptr(lse),
-                                          _ptr(delta), _ptr(dq_acc), _ptr(dk_out), _ptr(dv_out), _stream(stream)))
+    _check(lib().cp_attn_bwd_step_noalloc(ctypes.byref(p),
+                                          *_bwd_args(p, q, k, v, d_o, lse, delta, dq_acc, dk_out, dv_out),
+                                          _stream(stream)))

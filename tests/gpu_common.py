@@ -1,7 +1,6 @@
 """Shared helpers for the GPU parity tests (test infrastructure only)."""
 from __future__ import annotations
 
-import sys
 
 import numpy as np
 
@@ -12,8 +11,10 @@ LSE_RTOL = 1e-3      # |dLSE| <= 1e-3 * max(1, |LSE|)
 
 
 def note(msg: str) -> None:
-    """Print a progress line that names the case, flushed before the GPU work starts."""
-    print(f"[gpu-case] {msg}", file=sys.stderr, flush=True)
+    """Print a progress line that names the case, flushed before the GPU work starts
+    (to the real output, past pytest's capture)."""
+    from tests import live
+    live.line(f"[gpu-case] {msg}")
 
 
 def _to_device(bits: np.ndarray):

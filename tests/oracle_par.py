@@ -32,7 +32,6 @@ import concurrent.futures as cf
 import multiprocessing as mp
 import os
 import shutil
-import sys
 import tempfile
 import time
 import uuid
@@ -40,6 +39,7 @@ import uuid
 import numpy as np
 
 import oracle
+from tests import live
 from context_long_attention_amd import inputs
 
 _POOL = None
@@ -71,7 +71,7 @@ def pool(workers: int | None = None) -> cf.ProcessPoolExecutor:
 
 
 def _progress(what, done, total, t0):
-    print(f"[oracle] {what}: {done}/{total} heads, {time.time() - t0:.0f} s", file=sys.stderr, flush=True)
+    live.line(f"[oracle] {what}: {done}/{total} heads, {time.time() - t0:.0f} s")
 
 
 def shutdown():
@@ -285,6 +285,5 @@ class Backward:
                         dk[c0:c1] += dkb
                         dv[c0:c1] += dvb
             per_step.append(dkv)
-            print(f"[oracle] backward: step {t + 1}/{len(self.order)}, {time.time() - t0:.0f} s", file=sys.stderr,
-                  flush=True)
+            live.line(f"[oracle] backward: step {t + 1}/{len(self.order)}, {time.time() - t0:.0f} s")
         return dq, per_step, self.delta

@@ -465,3 +465,50 @@ def test_binding_refuses_strided_tensors():
     for bad in (a.t(), a[:, 1:3], torch.zeros((4, 6)).t().contiguous().t()):
         with pytest.raises(ValueError, match="not contiguous"):
             cpattn._ptr(bad)
+
+
+class _FakeDeviceTensor:
+    """Stands in for a dense GPU tensor: the binding's size checks read only these."""
+
+    def __init__(self, numel, elem, cuda=True):
+        self._n, self._e, self.is_cuda = numel, elem, cuda
+        self.shape, self.dtype = (numel,), f"{elem}-byte"
+
+    def numel(self):
+        return self._n
+
+    def element_size(self):
+        return self._e
+
+    def is_contiguous(self):
+        return True
+
+    def stride(self):
+        return (1,)
+
+    def data_ptr(self):
+        return 4096
+
+
+def test_binding_refuses_buffers_too_small_or_of_the_wrong_kind():
+    """The C ABI sees bare pointers, so the binding checks every device buffer
+    against the layout the call uses: element size, at least the implied number
+    of elements, on the GPU; a refused call never reaches the library."""
+    p = cpattn.make_problem(8, 2, 64, 0.125, 100, 70, [(0, 0, 100)], [(0, 0, 70)],
+                            [[cpattn.CP_MASK_DIAG_CAUSAL] * 2] * 2)
+    nq, nk, nl = 100 * 8 * 64, 70 * 2 * 64, 8 * 100
+    good = dict(q=_FakeDeviceTensor(nq, 2), k=_FakeDeviceTensor(nk, 2), v=_FakeDeviceTensor(nk, 2),
+                o=_FakeDeviceTensor(nq, 4), lse=_FakeDeviceTensor(nl, 4))
+    assert all(x is not None for x in cpattn._fwd_args(p, tile_map=None, **good)[:5])
+    for name, bad in [("q", _FakeDeviceTensor(nq - 1, 2)), ("k", _FakeDeviceTensor(nk, 4)),
+                      ("o", _FakeDeviceTensor(nq, 2)), ("lse", _FakeDeviceTensor(nl - 8, 4)),
+                      ("v", _FakeDeviceTensor(nk, 2, cuda=False))]:
+        with pytest.raises(ValueError, match=name):
+            cpattn._fwd_args(p, tile_map=None, **dict(good, **{name: bad}))
+    bwd = dict(q=good["q"], k=good["k"], v=good["v"], d_o=_FakeDeviceTensor(nq, 2), lse=good["lse"],
+               delta=_FakeDeviceTensor(nl, 4), dq=_FakeDeviceTensor(nq, 4), dk=_FakeDeviceTensor(nk, 4),
+               dv=_FakeDeviceTensor(nk, 4))
+    assert all(x is not None for x in cpattn._bwd_args(p, **bwd))
+    for name in ("delta", "dq", "dk"):
+        with pytest.raises(ValueError):
+            cpattn._bwd_args(p, **dict(bwd, **{name: _FakeDeviceTensor(10, 4)}))

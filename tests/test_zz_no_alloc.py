@@ -5,6 +5,8 @@ splits whose workspace fits the library's fixed scratch and at the library's
 own choice: the same bits as the workspace entry point (whose workspace is
 pre-filled with NaN) and the oracle's values within the parity tolerance.  A
 split whose workspace exceeds the scratch is refused before any launch."""
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -91,10 +93,14 @@ def test_noalloc_refuses_a_split_beyond_its_scratch():
     p = cpattn.make_problem(8, 8, 128, 0.1, 64, 1280, [(0, 5000, 64)], [(0, 0, 1280)], [[F, S_], [S_, S_]],
                             kv_split=8)
     assert cpattn.cp_bwd_workspace_size(p, 8) == 70 * (1 << 20)
+    # straight through the C entry point with a dummy buffer: the refusal comes
+    # before any pointer is used (the Python binding would refuse the dummy first)
     t = torch.empty(16, device="cuda")
-    with pytest.raises(cpattn.CpError) as e:
-        cpattn.cp_attn_bwd_step_noalloc(p, t, t, t, t, t, t, t, t, t)
-    assert e.value.status == cpattn.CP_ERR_INVALID_ARG
-    assert "no-alloc" in str(e.value)
+    ptr = ctypes.c_void_p(t.data_ptr())
+    st = cpattn.lib().cp_attn_bwd_step_noalloc(ctypes.byref(p), *([ptr] * 9),
+                                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == cpattn.CP_ERR_INVALID_ARG
+    assert "no-alloc" in cpattn.lib().cp_last_error().decode()
     p.kv_split = 4  # 3 x 80 x 128 KiB = 30 MiB fits
     assert cpattn.cp_bwd_workspace_size(p, 4) <= 64 * (1 << 20)
